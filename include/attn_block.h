@@ -1,0 +1,185 @@
+/*
+ * attn_block.h -- C ABI of libattnblock.so: forward pass of a non-causal
+ * multi-head self-attention block on AMD Instinct MI355X (gfx950), and the
+ * one-GPU share of context-parallel attention (partial results over K/V
+ * blocks, merged by log-sum-exp).
+ *
+ * What is computed (the definitions the library follows):
+ *   - The block: Q = X W_Q, K = X W_K, V = X W_V; split into heads; scaled
+ *     dot-product attention per head; concatenate the heads and multiply by
+ *     W_O. ["Tensor Parallelism: Sharding Weights for Parallel Layer
+ *     Execution", section 3 "Parallelizing the Multi-Head Attention Block";
+ *     Y = X A for a linear layer, section 1.]
+ *   - The query is pre-scaled before the QK^T product (the tensor named
+ *     q_scaled), here by 1/sqrt(head_dim); the block has hidden 4096 with 32
+ *     heads of 128 and an activation of shape (sequence, batch, hidden) in
+ *     fp16. ["Multi-Device Attention Inference with TensorRT", "What is
+ *     hint.json?" and "Generating the ONNX Models", Step 1.]
+ *   - Attention is bidirectional (no causal mask). A context-parallel rank
+ *     keeps its own Q slice and attends either to the gathered full K/V
+ *     (AllGather KV) or to K/V streamed in blocks whose results are combined
+ *     by online softmax (Ring Attention). [News summary of "Scaling AI
+ *     Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+ *     Inference Support", section on the three context-parallel
+ *     implementations.]
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, borrowed: the caller owns them
+ *     and keeps them valid until the work enqueued on `stream` completes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream); nothing blocks the host except attn_block_create and
+ *     attn_block_destroy, as stated there.
+ *   - Arguments are validated before any HIP call. A non-OK status means
+ *     nothing was enqueued (ATTN_E_HIP: a launch was rejected; earlier
+ *     launches of the same call may have been enqueued). attn_last_error()
+ *     returns a thread-local description of the last non-OK status.
+ *   - Faults while the kernels run surface at the caller's next
+ *     synchronisation. NaN/Inf inputs are not errors; they propagate.
+ *   - Strides and sizes are in ELEMENTS of the tensor's dtype. Floating point
+ *     arithmetic accumulates in fp32; ATTN_F16 tensors are IEEE binary16.
+ *   - LSE values are natural-log, fp32: lse = m + ln(sum_j exp(s_j - m)).
+ *   - No exception, abort or exit crosses this interface.
+ */
+#ifndef ATTN_BLOCK_H
+#define ATTN_BLOCK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_E_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment */
+    ATTN_E_UNSUPPORTED = 2, /* valid but not implemented (head_dim, batch, dtype) */
+    ATTN_E_OOM = 3,         /* device allocation failed (create only) */
+    ATTN_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} attn_status_t;
+
+typedef enum {
+    ATTN_F16 = 0, /* IEEE binary16; head_dim 128 */
+    ATTN_F32 = 1  /* IEEE binary32; head_dim 64 or 128 */
+} attn_dtype_t;
+
+/* Opaque block: packed weights plus the workspace of one forward pass. */
+typedef struct attn_block attn_block_t;
+
+/* Leading dimension (row stride) of a head-major V^T tensor for `seq` keys:
+ * seq rounded up to a multiple of 8, so every row starts 16-byte aligned. */
+#define ATTN_VT_LD(seq) ((((int64_t)(seq)) + 7) / 8 * 8)
+
+/*
+ * Optional taps of attn_block_forward: caller-owned device buffers that
+ * replace the block's internal intermediates (so tapping costs no copy).
+ * Every field may be NULL. Layouts, with S = seq, H = heads, d = head_dim,
+ * h = H*d, elements of the block's dtype unless noted:
+ *   q_scaled  [H][S][d]   q_scaled = (X W_Q)/sqrt(d), head j = columns j*d..
+ *   k         [H][S][d]   K = X W_K, head-major
+ *   v_t       [H][d][ATTN_VT_LD(S)]  V = X W_V transposed per head (keys
+ *             contiguous); columns S..ld-1 of each row are padding
+ *   attn_out  [S][h]      concatenated head outputs before W_O
+ *   lse       [H][S]      fp32 natural-log LSE of every query row
+ *   qkv_only  non-zero: stop after the QKV projection (q_scaled, k, v_t are
+ *             written; attention and the output projection are skipped and
+ *             y is not written). This is how the rank share gets its inputs.
+ */
+typedef struct {
+    void *q_scaled;
+    void *k;
+    void *v_t;
+    void *attn_out;
+    float *lse;
+    int qkv_only;
+} attn_taps_t;
+
+/*
+ * attn_block_create -- pack the four projection weights into library-owned
+ * device memory and allocate the workspace for up to max_tokens rows.
+ *   out        receives the block (set to NULL on failure).
+ *   hidden     h = num_heads * head_dim; head_dim 128 for ATTN_F16,
+ *              64 or 128 for ATTN_F32.
+ *   wq,wk,wv,wo device [h][h] row-major in `dt`, applied as Y = X W (input
+ *              features along rows). Copied; the caller may free them once
+ *              this returns.
+ *   max_tokens largest seq*batch any forward will use (>= 1).
+ *   stream     used for the packing kernels; synchronised before return.
+ * Workspace: about 4 * max_tokens * h elements of `dt`.
+ * Errors: ATTN_E_INVALID_ARG (null, h != H*d, max_tokens < 1),
+ * ATTN_E_UNSUPPORTED (head_dim, dtype), ATTN_E_OOM, ATTN_E_HIP.
+ */
+attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, attn_dtype_t dt,
+                                const void *wq, const void *wk, const void *wv, const void *wo,
+                                int64_t max_tokens, hipStream_t stream);
+
+/*
+ * attn_block_forward -- y = Block(x) for an activation [seq][batch][hidden].
+ *   x, y   device [seq][batch][h] in the block's dtype, 16-byte aligned; x and
+ *          y must not overlap. y is not written when taps->qkv_only is set.
+ *   seq    0 <= seq*batch <= max_tokens; seq = 0 enqueues nothing.
+ *   batch  must be 1 (ATTN_E_UNSUPPORTED otherwise).
+ *   taps   NULL, or caller buffers for intermediates (attn_taps_t).
+ * Steps on `stream`: QKV projection with the head split and the 1/sqrt(d)
+ * pre-scale fused into its epilogue; attention of every query row over all
+ * seq keys; output projection. Not safe to run concurrently with another
+ * forward of the same block (the workspace is shared).
+ */
+attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int64_t seq,
+                                 int64_t batch, const attn_taps_t *taps, hipStream_t stream);
+
+/*
+ * attn_partial_forward -- attention of a query chunk against one block of
+ * keys/values, all heads: o_part = softmax(q_scaled K^T) V normalised within
+ * the block, and its LSE. With the block being all keys this is the
+ * AllGather-KV share; with K/V streamed in blocks it is one Ring step.
+ *   num_heads, head_dim, dt  as for the block (d = 128 for ATTN_F16).
+ *   q_scaled  element (j,i,c) at q_scaled[j*q_head_stride + i*head_dim + c],
+ *             i < sq; already multiplied by 1/sqrt(head_dim).
+ *   k         element (j,t,c) at k[j*k_head_stride + t*head_dim + c], t < skv.
+ *   v_t       element (j,c,t) at v_t[j*v_head_stride + c*v_row_stride + t]
+ *             (V transposed per head: keys contiguous).
+ *   o_part    fp32 [H][sq][d] (contiguous), normalised within the block.
+ *   lse_part  fp32 [H][sq] (contiguous), natural-log.
+ * Pointers 16-byte aligned; head strides and v_row_stride multiples of 8
+ * (ATTN_F16) or 4 (ATTN_F32); v_row_stride >= skv. sq = 0 enqueues nothing.
+ * skv = 0 writes o_part = 0 and lse_part = -inf (a block with no keys, which
+ * carries zero weight in attn_merge_lse).
+ */
+attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt,
+                                   const void *q_scaled, int64_t sq, int64_t q_head_stride,
+                                   const void *k, int64_t skv, int64_t k_head_stride,
+                                   const void *v_t, int64_t v_head_stride, int64_t v_row_stride,
+                                   float *o_part, float *lse_part, hipStream_t stream);
+
+/*
+ * attn_merge_lse -- combine n_parts partial results of the same query rows
+ * by log-sum-exp: with M = max_b lse_b, lse = M + ln sum_b exp(lse_b - M)
+ * and o = sum_b exp(lse_b - lse) o_b (online softmax across blocks).
+ * Parts are summed in index order 0..n_parts-1 (deterministic).
+ *   o_parts   fp32 [n_parts][H][sq][d] contiguous, each normalised in its block.
+ *   lse_parts fp32 [n_parts][H][sq] contiguous.
+ *   o_out     [sq][H*d] token-major in out_dt (the concatenated-heads layout
+ *             the output projection consumes).
+ *   lse_out   NULL or fp32 [H][sq].
+ * Rows whose parts all have lse = -inf get o = 0 and lse = -inf.
+ * Pointers 16-byte aligned (o_out 8-byte aligned for ATTN_F16).
+ */
+attn_status_t attn_merge_lse(int n_parts, int num_heads, int head_dim, int64_t sq,
+                             const float *o_parts, const float *lse_parts,
+                             void *o_out, attn_dtype_t out_dt, float *lse_out,
+                             hipStream_t stream);
+
+/* attn_block_destroy -- synchronise the block's device and free everything
+ * the block owns. NULL is a no-op. */
+void attn_block_destroy(attn_block_t *blk);
+
+/* attn_last_error -- thread-local, NUL-terminated text for the last non-OK
+ * status returned on this thread ("" if none). Valid until the next call. */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BLOCK_H */

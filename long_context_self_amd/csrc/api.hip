@@ -1,0 +1,316 @@
+// C ABI of libattnblock.so (declared in include/attn_block.h): argument
+// validation, block lifecycle (packed weights + workspace) and the enqueueing
+// of the kernels for each entry point. No exception or abort crosses it.
+
+#include <cmath>
+#include <cstring>
+
+#include "attn_block.h"
+#include "common.hpp"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+#define ATTN_API extern "C" __attribute__((visibility("default")))
+
+using namespace attnblk;
+
+struct attn_block {
+    int hidden, heads, head_dim, dt, device;
+    int64_t max_tokens;
+    void *w_qkv;  // fp16: [3h][h] = [W_Q|W_K|W_V]^T; fp32: [h][3h] = [W_Q|W_K|W_V]
+    void *w_o;    // fp16: [h][h] = W_O^T;           fp32: [h][h] = W_O
+    void *ws_q, *ws_k, *ws_vt, *ws_o;
+};
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t set_error(int status, const char *msg) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+    return static_cast<attn_status_t>(status);
+}
+
+attn_status_t report(const Check &c) {
+    if (c.status == kOk) return ATTN_OK;
+    return set_error(c.status, c.msg);
+}
+
+attn_status_t hip_fail(const char *where, hipError_t e) {
+    char buf[512];
+    std::snprintf(buf, sizeof(buf), "%s: %s", where, hipGetErrorString(e));
+    return set_error(kHip, buf);
+}
+
+#define HIP_TRY(where, expr)                            \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess) return hip_fail(where, e_); \
+    } while (0)
+
+void free_block(attn_block *b) {
+    if (!b) return;
+    void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    delete b;
+}
+
+}  // namespace
+
+ATTN_API const char *attn_last_error(void) { return g_last_error; }
+
+ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, attn_dtype_t dt,
+                                         const void *wq, const void *wk, const void *wv, const void *wo,
+                                         int64_t max_tokens, hipStream_t stream) {
+    Check c = validate_create(out == nullptr, hidden, num_heads, (int)dt, wq, wk, wv, wo, max_tokens);
+    if (c.status != kOk) {
+        if (out) *out = nullptr;
+        return report(c);
+    }
+    *out = nullptr;
+    attn_block *b = new (std::nothrow) attn_block();
+    if (!b) return set_error(kOom, "attn_block_create: host allocation failed");
+    std::memset(b, 0, sizeof(*b));
+    b->hidden = hidden;
+    b->heads = num_heads;
+    b->head_dim = hidden / num_heads;
+    b->dt = (int)dt;
+    b->max_tokens = max_tokens;
+    hipError_t e = hipGetDevice(&b->device);
+    if (e != hipSuccess) {
+        free_block(b);
+        return hip_fail("attn_block_create: hipGetDevice", e);
+    }
+    const size_t es = elem_size(b->dt);
+    const size_t h = hidden;
+    const size_t qk_bytes = (size_t)max_tokens * h * es;
+    const size_t vt_bytes = (size_t)ATTN_VT_LD(max_tokens) * h * es;
+    struct {
+        void **p;
+        size_t bytes;
+    } allocs[] = {{&b->w_qkv, 3 * h * h * es}, {&b->w_o, h * h * es}, {&b->ws_q, qk_bytes},
+                  {&b->ws_k, qk_bytes},        {&b->ws_vt, vt_bytes},  {&b->ws_o, qk_bytes}};
+    for (auto &a : allocs) {
+        e = hipMalloc(a.p, a.bytes);
+        if (e != hipSuccess) {
+            *a.p = nullptr;
+            free_block(b);
+            (void)hipGetLastError();
+            return set_error(kOom, "attn_block_create: device allocation failed");
+        }
+    }
+    const void *w3[3] = {wq, wk, wv};
+    if (b->dt == kF16) {
+        for (int r = 0; r < 3; ++r) {
+            e = launch_transpose_f16(static_cast<const _Float16 *>(w3[r]), hidden, hidden,
+                                     static_cast<_Float16 *>(b->w_qkv) + (size_t)r * h * h, hidden, stream);
+            if (e != hipSuccess) break;
+        }
+        if (e == hipSuccess)
+            e = launch_transpose_f16(static_cast<const _Float16 *>(wo), hidden, hidden,
+                                     static_cast<_Float16 *>(b->w_o), hidden, stream);
+    } else {
+        for (int r = 0; r < 3 && e == hipSuccess; ++r)
+            e = hipMemcpy2DAsync(static_cast<char *>(b->w_qkv) + r * h * es, 3 * h * es, w3[r], h * es, h * es, h,
+                                 hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(b->w_o, wo, h * h * es, hipMemcpyDeviceToDevice, stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        free_block(b);
+        return hip_fail("attn_block_create: weight packing", e);
+    }
+    *out = b;
+    return ATTN_OK;
+}
+
+ATTN_API void attn_block_destroy(attn_block_t *blk) {
+    if (!blk) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(blk->device);
+    (void)hipDeviceSynchronize();
+    free_block(blk);
+    (void)hipSetDevice(cur);
+}
+
+ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int64_t seq, int64_t batch,
+                                          const attn_taps_t *taps, hipStream_t stream) {
+    TapsView tv{};
+    if (taps) tv = TapsView{taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->lse, taps->qkv_only};
+    Check c = validate_forward(blk == nullptr, blk ? blk->dt : 0, blk ? blk->hidden : 0,
+                               blk ? blk->max_tokens : 0, x, y, seq, batch, taps ? &tv : nullptr);
+    if (c.status != kOk) return report(c);
+    if (seq == 0) return ATTN_OK;
+    const int S = (int)(seq * batch);
+    const int h = blk->hidden, d = blk->head_dim, H = blk->heads;
+    const int64_t vt_ld = ATTN_VT_LD(S);
+    const float q_scale = (float)(1.0 / std::sqrt((double)d));
+    void *q = (taps && taps->q_scaled) ? taps->q_scaled : blk->ws_q;
+    void *k = (taps && taps->k) ? taps->k : blk->ws_k;
+    void *vt = (taps && taps->v_t) ? taps->v_t : blk->ws_vt;
+    void *o = (taps && taps->attn_out) ? taps->attn_out : blk->ws_o;
+    float *lse = taps ? taps->lse : nullptr;
+    const bool qkv_only = taps && taps->qkv_only;
+
+    if (blk->dt == kF16) {
+        GemmArgs g{};
+        g.a = static_cast<const _Float16 *>(x);
+        g.lda = h;
+        g.b = static_cast<const _Float16 *>(blk->w_qkv);
+        g.ldb = h;
+        g.M = S;
+        g.N = 3 * h;
+        g.K = h;
+        g.mode = kQkv;
+        g.q = static_cast<_Float16 *>(q);
+        g.k = static_cast<_Float16 *>(k);
+        g.vt = static_cast<_Float16 *>(vt);
+        g.vt_ld = vt_ld;
+        g.hidden = h;
+        g.head_dim = d;
+        g.q_scale = q_scale;
+        HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f16(g, stream));
+        if (qkv_only) return ATTN_OK;
+        FlashArgs fa{};
+        fa.q = g.q;
+        fa.k = g.k;
+        fa.vt = g.vt;
+        fa.q_head_stride = (int64_t)S * d;
+        fa.k_head_stride = (int64_t)S * d;
+        fa.v_head_stride = (int64_t)d * vt_ld;
+        fa.v_row_stride = vt_ld;
+        fa.sq = S;
+        fa.skv = S;
+        fa.num_heads = H;
+        fa.o16 = static_cast<_Float16 *>(o);
+        fa.o16_ld = h;
+        fa.lse = lse;
+        HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
+        GemmArgs go{};
+        go.a = static_cast<const _Float16 *>(o);
+        go.lda = h;
+        go.b = static_cast<const _Float16 *>(blk->w_o);
+        go.ldb = h;
+        go.M = S;
+        go.N = h;
+        go.K = h;
+        go.mode = kPlain;
+        go.c = static_cast<_Float16 *>(y);
+        go.ldc = h;
+        HIP_TRY("attn_block_forward: output projection", launch_gemm_f16(go, stream));
+    } else {
+        GemmArgsF32 g{};
+        g.a = static_cast<const float *>(x);
+        g.lda = h;
+        g.w = static_cast<const float *>(blk->w_qkv);
+        g.ldw = 3 * h;
+        g.M = S;
+        g.N = 3 * h;
+        g.K = h;
+        g.mode = kQkv;
+        g.q = static_cast<float *>(q);
+        g.k = static_cast<float *>(k);
+        g.vt = static_cast<float *>(vt);
+        g.vt_ld = vt_ld;
+        g.hidden = h;
+        g.head_dim = d;
+        g.q_scale = q_scale;
+        HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f32(g, stream));
+        if (qkv_only) return ATTN_OK;
+        FlashArgsF32 fa{};
+        fa.q = g.q;
+        fa.k = g.k;
+        fa.vt = g.vt;
+        fa.q_head_stride = (int64_t)S * d;
+        fa.k_head_stride = (int64_t)S * d;
+        fa.v_head_stride = (int64_t)d * vt_ld;
+        fa.v_row_stride = vt_ld;
+        fa.sq = S;
+        fa.skv = S;
+        fa.num_heads = H;
+        fa.head_dim = d;
+        fa.otok = static_cast<float *>(o);
+        fa.otok_ld = h;
+        fa.lse = lse;
+        HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f32(fa, stream));
+        GemmArgsF32 go{};
+        go.a = static_cast<const float *>(o);
+        go.lda = h;
+        go.w = static_cast<const float *>(blk->w_o);
+        go.ldw = h;
+        go.M = S;
+        go.N = h;
+        go.K = h;
+        go.mode = kPlain;
+        go.c = static_cast<float *>(y);
+        go.ldc = h;
+        HIP_TRY("attn_block_forward: output projection", launch_gemm_f32(go, stream));
+    }
+    return ATTN_OK;
+}
+
+ATTN_API attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
+                                            int64_t sq, int64_t q_head_stride, const void *k, int64_t skv,
+                                            int64_t k_head_stride, const void *v_t, int64_t v_head_stride,
+                                            int64_t v_row_stride, float *o_part, float *lse_part,
+                                            hipStream_t stream) {
+    Check c = validate_partial(num_heads, head_dim, (int)dt, q_scaled, sq, q_head_stride, k, skv, k_head_stride,
+                               v_t, v_head_stride, v_row_stride, o_part, lse_part);
+    if (c.status != kOk) return report(c);
+    if (sq == 0) return ATTN_OK;
+    if (dt == ATTN_F16) {
+        FlashArgs fa{};
+        fa.q = static_cast<const _Float16 *>(q_scaled);
+        fa.k = static_cast<const _Float16 *>(k);
+        fa.vt = static_cast<const _Float16 *>(v_t);
+        fa.q_head_stride = q_head_stride;
+        fa.k_head_stride = k_head_stride;
+        fa.v_head_stride = v_head_stride;
+        fa.v_row_stride = v_row_stride;
+        fa.sq = (int)sq;
+        fa.skv = (int)skv;
+        fa.num_heads = num_heads;
+        fa.o32 = o_part;
+        fa.lse = lse_part;
+        HIP_TRY("attn_partial_forward", launch_flash_fwd_f16(fa, stream));
+    } else {
+        FlashArgsF32 fa{};
+        fa.q = static_cast<const float *>(q_scaled);
+        fa.k = static_cast<const float *>(k);
+        fa.vt = static_cast<const float *>(v_t);
+        fa.q_head_stride = q_head_stride;
+        fa.k_head_stride = k_head_stride;
+        fa.v_head_stride = v_head_stride;
+        fa.v_row_stride = v_row_stride;
+        fa.sq = (int)sq;
+        fa.skv = (int)skv;
+        fa.num_heads = num_heads;
+        fa.head_dim = head_dim;
+        fa.o32 = o_part;
+        fa.lse = lse_part;
+        HIP_TRY("attn_partial_forward", launch_flash_fwd_f32(fa, stream));
+    }
+    return ATTN_OK;
+}
+
+ATTN_API attn_status_t attn_merge_lse(int n_parts, int num_heads, int head_dim, int64_t sq, const float *o_parts,
+                                      const float *lse_parts, void *o_out, attn_dtype_t out_dt, float *lse_out,
+                                      hipStream_t stream) {
+    Check c = validate_merge(n_parts, num_heads, head_dim, sq, o_parts, lse_parts, o_out, (int)out_dt, lse_out);
+    if (c.status != kOk) return report(c);
+    if (sq == 0) return ATTN_OK;
+    MergeArgs m{};
+    m.n_parts = n_parts;
+    m.num_heads = num_heads;
+    m.head_dim = head_dim;
+    m.sq = sq;
+    m.o_parts = o_parts;
+    m.lse_parts = lse_parts;
+    m.o_out = o_out;
+    m.out_f16 = out_dt == ATTN_F16;
+    m.lse_out = lse_out;
+    HIP_TRY("attn_merge_lse", launch_lse_merge(m, stream));
+    return ATTN_OK;
+}

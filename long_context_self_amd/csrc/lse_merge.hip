@@ -1,0 +1,77 @@
+// Log-sum-exp merge of per-block partial attention results (the combine step
+// of the online softmax that Ring Attention streams K/V with; news summary of
+// "Scaling AI Inference Across Multiple GPUs Using NVIDIA TensorRT with
+// Multi-Device Inference Support", three context-parallel implementations):
+//   M = max_b lse_b, w_b = exp(lse_b - M), lse = M + ln sum_b w_b,
+//   o = (sum_b w_b o_b) / sum_b w_b.
+// Output rows are written token-major [sq][H*d] -- the concatenated-heads
+// layout the output projection reads ("Tensor Parallelism: Sharding Weights
+// for Parallel Layer Execution", section 3).
+//
+// HBM-bound: each thread owns four consecutive head dimensions of one
+// (head, query) row, so every part is read in 16-byte coalesced chunks and
+// each part's LSE is read once per row from cache. Parts are summed in index
+// order, so the result is deterministic.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attnblk {
+
+namespace {
+
+__global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
+    const int tpr = a.head_dim / 4;  // threads per row
+    const int rows_per_block = 256 / tpr;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / tpr;
+    const int t = threadIdx.x % tpr;
+    const int64_t nrows = (int64_t)a.num_heads * a.sq;
+    if (row >= nrows) return;
+    const int head = (int)(row / a.sq);
+    const int64_t q = row % a.sq;
+    const int64_t part_stride_o = nrows * a.head_dim;
+
+    float m = -INFINITY;
+    for (int b = 0; b < a.n_parts; ++b) m = fmaxf(m, a.lse_parts[b * nrows + row]);
+
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse;
+    if (m == -INFINITY) {
+        lse = -INFINITY;
+    } else {
+        float total = 0.0f;
+        for (int b = 0; b < a.n_parts; ++b) {
+            const float w = expf(a.lse_parts[b * nrows + row] - m);
+            total += w;
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(a.o_parts + b * part_stride_o +
+                                                                  row * a.head_dim + 4 * t);
+            acc += w * v;
+        }
+        acc *= 1.0f / total;
+        lse = m + logf(total);
+    }
+    const int64_t ocol = (int64_t)head * a.head_dim + 4 * t;
+    const int64_t ld = (int64_t)a.num_heads * a.head_dim;
+    if (a.out_f16) {
+        half4 hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[r] = (half_t)acc[r];
+        *reinterpret_cast<half4 *>(reinterpret_cast<half_t *>(a.o_out) + q * ld + ocol) = hv;
+    } else {
+        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(a.o_out) + q * ld + ocol) = acc;
+    }
+    if (a.lse_out && t == 0) a.lse_out[row] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream) {
+    const int64_t nrows = (int64_t)a.num_heads * a.sq;
+    if (nrows <= 0) return hipSuccess;
+    const int rows_per_block = 256 / (a.head_dim / 4);
+    const int64_t blocks = (nrows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(lse_merge, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace attnblk

@@ -1,0 +1,158 @@
+// Argument validation for every C entry point. Pure C++ with no HIP calls, so
+// a failed check provably enqueues nothing, and the checks can be compiled
+// and tested on a host without a GPU.
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace attnblk {
+
+// Mirrors attn_status_t / attn_dtype_t of include/attn_block.h.
+enum Status { kOk = 0, kInvalid = 1, kUnsupported = 2, kOom = 3, kHip = 4 };
+enum Dtype { kF16 = 0, kF32 = 1 };
+
+constexpr int64_t kMaxTokens = int64_t(1) << 24;  // per forward / per partial side
+constexpr int kMaxHidden = 32768;
+constexpr int kMaxParts = 4096;
+
+struct Check {
+    int status;
+    char msg[256];
+};
+
+inline Check ok() {
+    Check c;
+    c.status = kOk;
+    c.msg[0] = '\0';
+    return c;
+}
+
+inline Check fail(int status, const char *fmt, ...) {
+    Check c;
+    c.status = status;
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(c.msg, sizeof(c.msg), fmt, ap);
+    va_end(ap);
+    return c;
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int elem_size(int dt) { return dt == kF16 ? 2 : 4; }
+inline bool dtype_known(int dt) { return dt == kF16 || dt == kF32; }
+inline bool head_dim_supported(int dt, int d) { return dt == kF16 ? d == 128 : (d == 64 || d == 128); }
+// Element count alignment of strides used by 16-byte vector accesses.
+inline int64_t vec_elems(int dt) { return dt == kF16 ? 8 : 4; }
+
+inline bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+inline Check validate_create(bool out_null, int hidden, int num_heads, int dt, const void *wq,
+                             const void *wk, const void *wv, const void *wo, int64_t max_tokens) {
+    if (out_null) return fail(kInvalid, "attn_block_create: out is NULL");
+    if (!dtype_known(dt)) return fail(kInvalid, "attn_block_create: unknown dtype %d", dt);
+    if (num_heads < 1) return fail(kInvalid, "attn_block_create: num_heads %d < 1", num_heads);
+    if (hidden < 1 || hidden % num_heads != 0)
+        return fail(kInvalid, "attn_block_create: hidden %d is not a multiple of num_heads %d", hidden,
+                    num_heads);
+    if (hidden > kMaxHidden) return fail(kUnsupported, "attn_block_create: hidden %d > %d", hidden, kMaxHidden);
+    const int d = hidden / num_heads;
+    if (!head_dim_supported(dt, d))
+        return fail(kUnsupported, "attn_block_create: head_dim %d not supported for dtype %d", d, dt);
+    if (!wq || !wk || !wv || !wo) return fail(kInvalid, "attn_block_create: a weight pointer is NULL");
+    if (!aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(wo, 16))
+        return fail(kInvalid, "attn_block_create: weights must be 16-byte aligned");
+    if (max_tokens < 1) return fail(kInvalid, "attn_block_create: max_tokens %lld < 1", (long long)max_tokens);
+    if (max_tokens > kMaxTokens)
+        return fail(kUnsupported, "attn_block_create: max_tokens %lld > %lld", (long long)max_tokens,
+                    (long long)kMaxTokens);
+    return ok();
+}
+
+struct TapsView {
+    const void *q_scaled, *k, *v_t, *attn_out;
+    const float *lse;
+    int qkv_only;
+};
+
+inline Check validate_forward(bool blk_null, int dt, int hidden, int64_t max_tokens, const void *x,
+                              const void *y, int64_t seq, int64_t batch, const TapsView *taps) {
+    if (blk_null) return fail(kInvalid, "attn_block_forward: blk is NULL");
+    if (batch < 1) return fail(kInvalid, "attn_block_forward: batch %lld < 1", (long long)batch);
+    if (batch != 1) return fail(kUnsupported, "attn_block_forward: batch %lld != 1", (long long)batch);
+    if (seq < 0) return fail(kInvalid, "attn_block_forward: seq %lld < 0", (long long)seq);
+    if (seq * batch > max_tokens)
+        return fail(kInvalid, "attn_block_forward: seq*batch %lld exceeds max_tokens %lld",
+                    (long long)(seq * batch), (long long)max_tokens);
+    if (seq == 0) return ok();
+    const bool qkv_only = taps && taps->qkv_only;
+    if (!x) return fail(kInvalid, "attn_block_forward: x is NULL");
+    if (!qkv_only && !y) return fail(kInvalid, "attn_block_forward: y is NULL");
+    if (!aligned(x, 16) || (y && !aligned(y, 16)))
+        return fail(kInvalid, "attn_block_forward: x and y must be 16-byte aligned");
+    const int64_t bytes = seq * batch * hidden * elem_size(dt);
+    if (y && !qkv_only && overlap(x, bytes, y, bytes)) return fail(kInvalid, "attn_block_forward: x and y overlap");
+    if (taps) {
+        const void *p16[4] = {taps->q_scaled, taps->k, taps->v_t, taps->attn_out};
+        for (const void *p : p16)
+            if (p && !aligned(p, 16)) return fail(kInvalid, "attn_block_forward: tap buffers must be 16-byte aligned");
+        if (taps->lse && !aligned(taps->lse, 4)) return fail(kInvalid, "attn_block_forward: lse tap misaligned");
+    }
+    return ok();
+}
+
+inline Check validate_partial(int num_heads, int head_dim, int dt, const void *q, int64_t sq, int64_t qhs,
+                              const void *k, int64_t skv, int64_t khs, const void *vt, int64_t vhs,
+                              int64_t vrs, const float *o_part, const float *lse_part) {
+    if (!dtype_known(dt)) return fail(kInvalid, "attn_partial_forward: unknown dtype %d", dt);
+    if (num_heads < 1) return fail(kInvalid, "attn_partial_forward: num_heads %d < 1", num_heads);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "attn_partial_forward: head_dim %d not supported for dtype %d", head_dim, dt);
+    if (sq < 0 || skv < 0) return fail(kInvalid, "attn_partial_forward: negative sq or skv");
+    if (sq > kMaxTokens || skv > kMaxTokens)
+        return fail(kUnsupported, "attn_partial_forward: sq or skv above %lld", (long long)kMaxTokens);
+    if (sq == 0) return ok();
+    if (!q || !o_part || !lse_part) return fail(kInvalid, "attn_partial_forward: q, o_part or lse_part is NULL");
+    if (skv > 0 && (!k || !vt)) return fail(kInvalid, "attn_partial_forward: k or v_t is NULL");
+    if (!aligned(q, 16) || !aligned(o_part, 16) || (skv > 0 && (!aligned(k, 16) || !aligned(vt, 16))))
+        return fail(kInvalid, "attn_partial_forward: q, k, v_t and o_part must be 16-byte aligned");
+    if (!aligned(lse_part, 4)) return fail(kInvalid, "attn_partial_forward: lse_part misaligned");
+    const int64_t ve = vec_elems(dt);
+    if (qhs < 0 || khs < 0 || vhs < 0 || vrs < 0)
+        return fail(kInvalid, "attn_partial_forward: negative stride");
+    if (qhs % ve || khs % ve || vhs % ve || vrs % ve)
+        return fail(kInvalid, "attn_partial_forward: head strides and v_row_stride must be multiples of %lld",
+                    (long long)ve);
+    if (num_heads > 1 && qhs < sq * head_dim)
+        return fail(kInvalid, "attn_partial_forward: q_head_stride %lld < sq*head_dim", (long long)qhs);
+    if (skv > 0) {
+        if (vrs < skv) return fail(kInvalid, "attn_partial_forward: v_row_stride %lld < skv", (long long)vrs);
+        if (num_heads > 1 && (khs < skv * head_dim || vhs < head_dim * vrs))
+            return fail(kInvalid, "attn_partial_forward: k/v head strides smaller than one head");
+    }
+    return ok();
+}
+
+inline Check validate_merge(int n_parts, int num_heads, int head_dim, int64_t sq, const float *o_parts,
+                            const float *lse_parts, const void *o_out, int out_dt, const float *lse_out) {
+    if (n_parts < 1) return fail(kInvalid, "attn_merge_lse: n_parts %d < 1", n_parts);
+    if (n_parts > kMaxParts) return fail(kUnsupported, "attn_merge_lse: n_parts %d > %d", n_parts, kMaxParts);
+    if (!dtype_known(out_dt)) return fail(kInvalid, "attn_merge_lse: unknown dtype %d", out_dt);
+    if (num_heads < 1) return fail(kInvalid, "attn_merge_lse: num_heads %d < 1", num_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(kUnsupported, "attn_merge_lse: head_dim %d not supported", head_dim);
+    if (sq < 0) return fail(kInvalid, "attn_merge_lse: sq %lld < 0", (long long)sq);
+    if (sq > kMaxTokens) return fail(kUnsupported, "attn_merge_lse: sq above %lld", (long long)kMaxTokens);
+    if (sq == 0) return ok();
+    if (!o_parts || !lse_parts || !o_out) return fail(kInvalid, "attn_merge_lse: NULL input or output");
+    if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(o_out, out_dt == kF16 ? 8 : 16) ||
+        (lse_out && !aligned(lse_out, 4)))
+        return fail(kInvalid, "attn_merge_lse: misaligned pointer");
+    return ok();
+}
+
+}  // namespace attnblk

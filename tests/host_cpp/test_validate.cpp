@@ -1,0 +1,66 @@
+// Host-only unit test of the argument validation layer (no HIP, no GPU).
+// Built with g++ under AddressSanitizer and UBSan by tests/test_host_validate.py.
+#include <cstdio>
+#include <cstring>
+
+#include "validate.hpp"
+
+using namespace attnblk;
+
+static int failures = 0;
+#define EXPECT(cond)                                                  \
+    do {                                                              \
+        if (!(cond)) {                                                \
+            std::printf("FAIL line %d: %s\n", __LINE__, #cond);       \
+            ++failures;                                               \
+        }                                                             \
+    } while (0)
+
+int main() {
+    const void *P = reinterpret_cast<const void *>(0x1000);
+    const float *F = reinterpret_cast<const float *>(0x1000);
+    // create
+    EXPECT(validate_create(false, 4096, 32, kF16, P, P, P, P, 65536).status == kOk);
+    EXPECT(validate_create(false, 256, 4, kF32, P, P, P, P, 256).status == kOk);
+    EXPECT(validate_create(true, 4096, 32, kF16, P, P, P, P, 16).status == kInvalid);
+    EXPECT(validate_create(false, 4096, 0, kF16, P, P, P, P, 16).status == kInvalid);
+    EXPECT(validate_create(false, 4096, 64, kF16, P, P, P, P, 16).status == kUnsupported);
+    EXPECT(validate_create(false, 256, 8, kF32, P, P, P, P, 16).status == kUnsupported);
+    EXPECT(validate_create(false, 4096, 32, 5, P, P, P, P, 16).status == kInvalid);
+    EXPECT(validate_create(false, 4096, 32, kF16, P, P, P, P, kMaxTokens + 1).status == kUnsupported);
+    Check c = validate_create(false, 4096, 32, kF16, nullptr, P, P, P, 16);
+    EXPECT(c.status == kInvalid && std::strstr(c.msg, "NULL"));
+    // forward
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, reinterpret_cast<const char *>(P) + (1 << 24), 1024, 1,
+                            nullptr).status == kOk);
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, P, 1024, 1, nullptr).status == kInvalid);  // overlap
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 1025, 1, nullptr).status == kInvalid);
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 16, 2, nullptr).status == kUnsupported);
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 16, 0, nullptr).status == kInvalid);
+    EXPECT(validate_forward(false, kF16, 4096, 1024, nullptr, nullptr, 0, 1, nullptr).status == kOk);
+    TapsView t{};
+    t.qkv_only = 1;
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 16, 1, &t).status == kOk);
+    t.k = reinterpret_cast<const char *>(P) + 2;
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 16, 1, &t).status == kInvalid);
+    // partial
+    EXPECT(validate_partial(32, 128, kF16, P, 4096, 4096 * 128, P, 4096, 32768 * 128, P, 128 * 32768, 32768, F,
+                            F).status == kOk);
+    EXPECT(validate_partial(32, 128, kF16, P, 4096, 4096 * 128, P, 4096, 32768 * 128, P, 128 * 32768, 4000, F,
+                            F).status == kInvalid);
+    EXPECT(validate_partial(32, 128, kF16, P, 1, 128, P, 0, 0, nullptr, 0, 0, F, F).status == kOk);
+    EXPECT(validate_partial(4, 64, kF32, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status == kOk);
+    EXPECT(validate_partial(4, 64, kF16, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status ==
+           kUnsupported);
+    // merge
+    EXPECT(validate_merge(8, 32, 128, 4096, F, F, P, kF16, nullptr).status == kOk);
+    EXPECT(validate_merge(0, 32, 128, 4096, F, F, P, kF16, nullptr).status == kInvalid);
+    EXPECT(validate_merge(8, 32, 128, 4096, F, F, reinterpret_cast<const char *>(P) + 4, kF16, nullptr).status ==
+           kInvalid);
+    EXPECT(validate_merge(kMaxParts + 1, 32, 128, 16, F, F, P, kF16, nullptr).status == kUnsupported);
+    // long messages are truncated, not overflowed
+    c = fail(kInvalid, "%s", std::string(1000, 'x').c_str());
+    EXPECT(std::strlen(c.msg) == sizeof(c.msg) - 1);
+    std::printf("%s (%d failures)\n", failures ? "FAILED" : "OK", failures);
+    return failures ? 1 : 0;
+}

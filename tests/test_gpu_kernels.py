@@ -1,0 +1,222 @@
+"""GPU parity of the attention kernel (attn_partial_forward) and the LSE merge
+(attn_merge_lse) against the fp64 oracle, at sizes that span several tiles
+with ragged tails, plus the method's degenerate cases and the GPU-only
+properties (split-merge vs unsplit, row-chunk bit-exactness, determinism)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_self_amd import binding as B
+from long_context_self_amd.synthetic import attention_inputs
+
+from .gpu_util import (REL_L2_F16, REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, partial, rel_l2, say,
+                       to_vt)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.lib()
+
+
+def _run(h, sq, skv, d=128, dtype=np.float16, seed=0, score_std=1.0):
+    q, k, v = attention_inputs(h, sq, skv, d, dtype=dtype, seed=seed, score_std=score_std)
+    tdt = torch.float16 if dtype == np.float16 else torch.float32
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2], dtype=tdt)
+    return (q, k, v), host(o), host(lse)
+
+
+@pytest.mark.parametrize("h,sq,skv", [(2, 300, 200), (3, 1000, 1000), (1, 257, 4097), (2, 64, 63)])
+def test_partial_f16_vs_oracle(h, sq, skv):
+    say(f"partial f16 H={h} sq={sq} skv={skv}")
+    (q, k, v), o, lse = _run(h, sq, skv)
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(o, o_ref, what="o_part")
+    assert_close(lse, lse_ref, what="lse_part")
+
+
+def test_partial_f16_peaked_scores_exercise_rescale():
+    # score std 8: running maxima keep growing by more than the 2^8 lazy-rescale threshold
+    say("partial f16 peaked scores")
+    (q, k, v), o, lse = _run(2, 500, 3000, score_std=8.0, seed=3)
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(o, o_ref, what="o_part peaked")
+    assert_close(lse, lse_ref, what="lse peaked")
+
+
+def test_partial_f16_increasing_keys_force_every_rescale():
+    # keys ordered so each tile's max exceeds the previous by far more than 2^8
+    say("partial f16 increasing scores")
+    h, sq, skv, d = 1, 64, 640, 128
+    rng = np.random.default_rng(5)
+    q = np.full((h, sq, d), 0.05, np.float16)
+    base = rng.standard_normal((h, skv, d)).astype(np.float32) * 0.1
+    ramp = np.linspace(0.0, 30.0, skv, dtype=np.float32)[None, :, None]
+    k = (base + ramp).astype(np.float16)
+    v = rng.standard_normal((h, skv, d)).astype(np.float16)
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(host(o), o_ref, what="o ramp")
+    assert_close(host(lse), lse_ref, what="lse ramp")
+
+
+def test_partial_zero_query_gives_mean_of_v():
+    say("zero query -> mean of V")
+    h, sq, skv, d = 2, 70, 333, 128
+    _, k, v = attention_inputs(h, sq, skv, d, seed=1)
+    q = np.zeros((h, sq, d), np.float16)
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    mean_v = v.astype(np.float64).mean(axis=1, keepdims=True)
+    assert_close(host(o), np.broadcast_to(mean_v, (h, sq, d)), rel=1e-5, mabs=1e-5, what="mean of V")
+    assert np.allclose(host(lse), np.log(skv), atol=1e-5)
+
+
+def test_partial_single_key_returns_its_value():
+    say("single key")
+    h, sq, skv, d = 2, 100, 1, 128
+    q, k, v = attention_inputs(h, sq, skv, d, seed=2)
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    # exp(s - m) of the only key is 1 up to the rounding of s*log2(e) in the
+    # exp2-domain softmax, so O equals that V row to fp32 rounding.
+    assert np.allclose(host(o), np.broadcast_to(v.astype(np.float64), (h, sq, d)), rtol=1e-6, atol=0)
+    score = np.einsum("hqd,hkd->hq", q.astype(np.float64), k.astype(np.float64))
+    assert np.allclose(host(lse), score, atol=1e-4)
+
+
+def test_partial_empty_kv_block():
+    say("skv = 0")
+    h, sq, d = 2, 50, 128
+    q = dev(attention_inputs(h, sq, 1, d)[0])
+    o = torch.full((h, sq, d), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.zeros((h, sq), dtype=torch.float32, device="cuda")
+    B.attn_partial_forward(h, d, q, sq, q.stride(0), None, 0, 0, None, 0, 0, o, lse)
+    assert np.all(host(o) == 0.0)
+    assert np.all(np.isneginf(host(lse)))
+
+
+def test_partial_single_query_row():
+    say("sq = 1")
+    (q, k, v), o, lse = _run(4, 1, 777, seed=4)
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(o, o_ref, what="o sq=1")
+    assert_close(lse, lse_ref, what="lse sq=1")
+
+
+def test_split_merge_equals_unsplit():
+    say("split-merge vs unsplit")
+    h, sq, skv, d = 3, 600, 2000, 128
+    q, k, v = attention_inputs(h, sq, skv, d, seed=6)
+    qd = dev(q)
+    vt_full = to_vt(v)
+    o_full, lse_full = partial(qd, dev(k), dev(vt_full), sq, skv, vt_full.shape[2])
+    cuts = [0, 512, 1000, 1001, 1600, 2000]  # uneven, with a size-1 block
+    n = len(cuts) - 1
+    o_parts = torch.empty((n, h, sq, d), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((n, h, sq), dtype=torch.float32, device="cuda")
+    for b, (a0, a1) in enumerate(zip(cuts[:-1], cuts[1:])):
+        vt = to_vt(np.ascontiguousarray(v[:, a0:a1]))
+        ob, lb = partial(qd, dev(np.ascontiguousarray(k[:, a0:a1])), dev(vt), sq, a1 - a0, vt.shape[2])
+        o_parts[b].copy_(ob)
+        lse_parts[b].copy_(lb)
+    o_m = torch.empty((sq, h * d), dtype=torch.float16, device="cuda")
+    lse_m = torch.empty((h, sq), dtype=torch.float32, device="cuda")
+    B.attn_merge_lse(n, h, d, sq, o_parts, lse_parts, o_m, torch.float16, lse_m)
+    o_m_heads = host(o_m).reshape(sq, h, d).transpose(1, 0, 2)
+    r = rel_l2(o_m_heads, host(o_full))
+    say(f"  merged vs unsplit rel_l2={r:.3e}")
+    assert r <= REL_L2_SPLIT
+    assert rel_l2(host(lse_m), host(lse_full)) <= 1e-6
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(o_m_heads, o_ref, what="merged vs oracle")
+    assert_close(host(lse_m), lse_ref, what="merged lse vs oracle")
+
+
+def test_merge_ignores_empty_parts_and_handles_all_empty():
+    say("merge with empty parts")
+    h, sq, d = 2, 40, 128
+    rng = np.random.default_rng(9)
+    o_parts = rng.standard_normal((3, h, sq, d)).astype(np.float32)
+    lse_parts = rng.standard_normal((3, h, sq)).astype(np.float32)
+    lse_parts[1] = -np.inf
+    o_out = torch.empty((sq, h * d), dtype=torch.float32, device="cuda")
+    lse_out = torch.empty((h, sq), dtype=torch.float32, device="cuda")
+    B.attn_merge_lse(3, h, d, sq, dev(o_parts), dev(lse_parts), o_out, torch.float32, lse_out)
+    o_ref, lse_ref = oracle.merge_partials(o_parts, lse_parts)
+    got = host(o_out).reshape(sq, h, d).transpose(1, 0, 2)
+    assert rel_l2(got, o_ref) <= 1e-6
+    assert rel_l2(host(lse_out), lse_ref) <= 1e-6
+    lse_parts[:] = -np.inf
+    B.attn_merge_lse(3, h, d, sq, dev(o_parts), dev(lse_parts), o_out, torch.float32, lse_out)
+    assert np.all(host(o_out) == 0.0) and np.all(np.isneginf(host(lse_out)))
+
+
+@pytest.mark.parametrize("a,b", [(256, 512), (100, 357), (999, 1000)])
+def test_row_chunk_is_bit_exact(a, b):
+    # Rows [a, b) run alone against the full K/V equal rows [a, b) of the full run.
+    say(f"row chunk [{a},{b}) bit-exact")
+    h, sq, skv, d = 2, 1000, 1500, 128
+    q, k, v = attention_inputs(h, sq, skv, d, seed=7)
+    kd, vt = dev(k), to_vt(v)
+    vtd = dev(vt)
+    o_full, lse_full = partial(dev(q), kd, vtd, sq, skv, vt.shape[2])
+    qc = dev(np.ascontiguousarray(q[:, a:b]))
+    o_c, lse_c = partial(qc, kd, vtd, b - a, skv, vt.shape[2])
+    assert torch.equal(o_c, o_full[:, a:b])
+    assert torch.equal(lse_c, lse_full[:, a:b])
+
+
+def test_two_runs_are_bit_identical():
+    say("determinism")
+    h, sq, skv, d = 4, 1024, 2048, 128
+    q, k, v = attention_inputs(h, sq, skv, d, seed=8)
+    vt = to_vt(v)
+    args = (dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    o1, l1 = partial(*args)
+    o2, l2 = partial(*args)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_partial_f32_vs_oracle(d):
+    say(f"partial f32 d={d}")
+    (q, k, v), o, lse = _run(4, 256, 300, d=d, dtype=np.float32, seed=10)
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(o, o_ref, rel=REL_L2_F32, mabs=1e-5, what="o f32")
+    assert_close(lse, lse_ref, rel=REL_L2_F32, mabs=1e-5, what="lse f32")
+
+
+def test_tiny_config_split_into_four_chunks_fp32():
+    # Tiny configuration: 4 heads of 64, 256 keys split into 4 chunks of 64,
+    # partials merged by LSE, against the oracle and the unsplit GPU result.
+    say("tiny fp32 4-chunk split")
+    h, s, d = 4, 256, 64
+    q, k, v = attention_inputs(h, s, s, d, dtype=np.float32, seed=0)
+    qd = dev(q)
+    vt_full = to_vt(v)
+    o_full, lse_full = partial(qd, dev(k), dev(vt_full), s, s, vt_full.shape[2], dtype=torch.float32)
+    o_parts = torch.empty((4, h, s, d), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((4, h, s), dtype=torch.float32, device="cuda")
+    for b in range(4):
+        kb = np.ascontiguousarray(k[:, 64 * b:64 * (b + 1)])
+        vtb = to_vt(np.ascontiguousarray(v[:, 64 * b:64 * (b + 1)]))
+        ob, lb = partial(qd, dev(kb), dev(vtb), s, 64, vtb.shape[2], dtype=torch.float32)
+        o_parts[b].copy_(ob)
+        lse_parts[b].copy_(lb)
+    o_m = torch.empty((s, h * d), dtype=torch.float32, device="cuda")
+    lse_m = torch.empty((h, s), dtype=torch.float32, device="cuda")
+    B.attn_merge_lse(4, h, d, s, o_parts, lse_parts, o_m, torch.float32, lse_m)
+    got = host(o_m).reshape(s, h, d).transpose(1, 0, 2)
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    assert_close(got, o_ref, rel=REL_L2_F32, mabs=1e-5, what="tiny merged vs oracle")
+    assert_close(host(lse_m), lse_ref, rel=REL_L2_F32, mabs=1e-5, what="tiny merged lse")
+    assert rel_l2(got, host(o_full)) <= REL_L2_SPLIT
