@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X self-attention block forward (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+
+A step is one forward of the block -- QKV projection (with the head split and
+the q_scaled pre-scale fused into its epilogue), attention over the full
+sequence, output projection -- on the headline workload: seq 8192, batch 1,
+hidden 4096, 32 heads of 128, fp16, non-causal, seeded synthetic inputs
+already resident in HBM. W untimed steps, then K timed steps bracketed by
+torch.cuda.synchronize(); HIP events recorded by the library between its
+kernels (the ``events`` tap) give per-kernel durations inside the timed
+region, on the stream the kernels run on.
+
+The same run also times, in the same way, the other workloads: seq 16384 /
+32768 / 65536 at hidden 4096, seq 8192 at hidden 8192 (64 heads), the
+context-parallel rank share (a 4096-row query chunk of seq 32768 against K/V in
+8 blocks of 4096, partials + LSE merge) and 6 stacked blocks at seq 32768.
+The CPU baseline is the fp64 oracle, timed on a bounded sample of the headline
+workload on this host's cores.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_F16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 2516.6: MI355X dense fp16 MFMA (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0                         # MI355X HBM3E, 8 TB/s
+
+METRIC = "ms/forward + attention TFLOP/s (frac of fp16 MFMA peak), 1 MI355X"
+
+# Latencies the pages report for TensorRT on one B200 (context, not a target).
+B200_CONTEXT = {
+    "hardware": "1x NVIDIA B200, TensorRT 11.0 via Triton, batch 1, end-to-end request latency (+-10%)",
+    "seq16384_h4096_ms": "480-724", "seq32768_h4096_ms": "1160", "seq65536_h4096_ms": "2224",
+    "seq8192_h8192_ms": "593-728", "six_stack_seq32768_ms": "1187-1388",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through the runtime torch already loaded (one runtime per process)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.L.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+        return arr
+
+    def record(self, ev, stream):
+        if self.L.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.L.hipEventDestroy(e)
+
+
+def block_flops(seq, h):
+    return {"qkv": 6.0 * seq * h * h, "attn": 4.0 * seq * seq * h, "oproj": 2.0 * seq * h * h}
+
+
+def stats(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(xs)), "min": float(xs.min()), "p90": float(np.percentile(xs, 90)),
+            "mean": float(xs.mean())}
+
+
+def run_block(torch, B, hip, seq, h, nh, layers, warmup, steps, seed=0):
+    """Time `steps` forwards of a stack of `layers` blocks; per-kernel times from the events tap."""
+    from long_context_self_amd.synthetic import block_inputs
+
+    x, ws = block_inputs(seq, h, layers, dtype=np.float16, seed=seed)
+    blocks = [B.AttnBlock(*(torch.from_numpy(w).cuda() for w in lw), num_heads=nh, max_tokens=seq) for lw in ws]
+    del ws
+    xd = torch.from_numpy(x).cuda()
+    del x
+    bufs = [torch.empty_like(xd), torch.empty_like(xd)]
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = hip.events(4 * layers * steps)
+    tot = hip.events(2)
+
+    def one(step_events):
+        cur = xd
+        for li, blk in enumerate(blocks):
+            taps = None
+            if step_events is not None:
+                base = ctypes.addressof(evs) + (step_events + 4 * li) * ctypes.sizeof(ctypes.c_void_p)
+                taps = B.Taps(None, None, None, None, None, 0, base)
+            out = bufs[li % 2]
+            blk.forward(cur, out, taps=taps)
+            cur = out
+        return cur
+
+    for _ in range(warmup):
+        one(None)
+    torch.cuda.synchronize()
+    hip.record(tot[0], stream)
+    for s in range(steps):
+        one(4 * layers * s)
+    hip.record(tot[1], stream)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(tot[0], tot[1])
+    k = {"qkv": [], "attn": [], "oproj": [], "step": []}
+    for s in range(steps):
+        e = [evs[4 * layers * s + i] for i in range(4 * layers)]
+        k["step"].append(hip.ms(e[0], e[4 * layers - 1]))
+        for li in range(layers):
+            b = 4 * li
+            k["qkv"].append(hip.ms(e[b], e[b + 1]))
+            k["attn"].append(hip.ms(e[b + 1], e[b + 2]))
+            k["oproj"].append(hip.ms(e[b + 2], e[b + 3]))
+    hip.destroy(evs)
+    hip.destroy(tot)
+    for blk in blocks:
+        blk.close()
+    del bufs, xd
+    torch.cuda.empty_cache()
+    return total_ms / steps, {n: stats(v) for n, v in k.items()}
+
+
+def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks=8, seed=0):
+    """Rank 0's share: its seq/8 query chunk against K/V streamed in 8 blocks
+    (partial + LSE per block, then one merge), inputs from the block's QKV taps."""
+    from long_context_self_amd.synthetic import block_inputs
+
+    d = h // nh
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
+    blk = B.AttnBlock(*(torch.from_numpy(w).cuda() for w in ws), num_heads=nh, max_tokens=seq)
+    ld = B.vt_ld(seq)
+    q = torch.empty((nh, seq, d), dtype=torch.float16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((nh, d, ld), dtype=torch.float16, device="cuda")
+    blk.forward(torch.from_numpy(x).cuda(), taps=B.Taps(q.data_ptr(), k.data_ptr(), vt.data_ptr(), None, None, 1,
+                                                           None))
+    torch.cuda.synchronize()
+    blk.close()
+    chunk = seq // ranks
+    o_parts = torch.empty((ranks, nh, chunk, d), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((ranks, nh, chunk), dtype=torch.float32, device="cuda")
+    o = torch.empty((chunk, h), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = hip.events(3 * steps)
+
+    def one(s):
+        if s is not None:
+            hip.record(evs[3 * s], stream)
+        for b in range(ranks):
+            B.attn_partial_forward(nh, d, q, chunk, seq * d, k[:, b * chunk:], chunk, seq * d,
+                                   vt[:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b])
+        if s is not None:
+            hip.record(evs[3 * s + 1], stream)
+        B.attn_merge_lse(ranks, nh, d, chunk, o_parts, lse_parts, o, torch.float16)
+        if s is not None:
+            hip.record(evs[3 * s + 2], stream)
+
+    for _ in range(warmup):
+        one(None)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        one(s)
+    torch.cuda.synchronize()
+    part = [hip.ms(evs[3 * s], evs[3 * s + 1]) for s in range(steps)]
+    merge = [hip.ms(evs[3 * s + 1], evs[3 * s + 2]) for s in range(steps)]
+    hip.destroy(evs)
+    flops = 4.0 * chunk * seq * h
+    merge_bytes = ranks * chunk * h * 4 + ranks * nh * chunk * 4 + chunk * h * 2
+    ps, ms_ = stats(part), stats(merge)
+    del q, k, vt, o_parts, lse_parts, o
+    torch.cuda.empty_cache()
+    return {
+        "workload": "rank share: 4096-row query chunk of seq 32768 vs K/V in 8 blocks of 4096, hidden 4096, 32 heads",
+        "ms": ps["median"] + ms_["median"], "partials_ms": ps, "merge_ms": ms_,
+        "attention_tflops": flops / (ps["median"] * 1e-3) / 1e12,
+        "attention_frac_of_peak": flops / (ps["median"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "merge_gbs": merge_bytes / (ms_["median"] * 1e-3) / 1e9,
+        "merge_frac_of_hbm": merge_bytes / (ms_["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "merge_bytes": merge_bytes,
+    }
+
+
+def cpu_baseline(seq=8192, h=4096, nh=32, rows=2048, seed=0):
+    """The fp64 oracle on a bounded sample of the headline workload: K and V
+    over all seq rows, and rows `rows` sampled query rows through attention and
+    the output projection (exact for those rows)."""
+    import oracle
+    from long_context_self_amd.synthetic import block_inputs, sample_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") == "openblas"]
+                    or [1])
+    except Exception:
+        cores = None
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
+    r = sample_rows(seq, rows, seed=seed)
+    t0 = time.perf_counter()
+    oracle.block_forward(x, *ws, nh, rows=r)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * seq * h * h + len(r) * (2.0 * h * h + 4.0 * seq * h + 2.0 * h * h)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"fp64 numpy oracle, seq {seq} hidden {h} 32 heads: K and V over all {seq} rows plus "
+                      f"{len(r)} sampled query rows through attention and W_O; value = algorithmic FLOPs of "
+                      f"that work / wall time"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library builds no "
+              f"multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from long_context_self_amd import binding as B
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    hip = Hip()
+    seq, h, nh = 8192, 4096, 32
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.float16, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    log(f"headline: seq {seq} hidden {h} heads {nh}, warmup {args.warmup}, steps {args.steps}")
+    ms, kern = run_block(torch, B, hip, seq, h, nh, 1, args.warmup, args.steps)
+    fl = block_flops(seq, h)
+    total_flops = sum(fl.values())
+    kernel_tflops = {n: fl[n] / (kern[n]["mean"] * 1e-3) / 1e12 for n in ("qkv", "attn", "oproj")}
+    dom = max(("qkv", "attn", "oproj"), key=lambda n: kern[n]["mean"])
+    names = {"qkv": "gemm_f16_nt (QKV projection, fused layout epilogue)",
+             "attn": "flash_fwd_f16_d128 (attention)", "oproj": "gemm_f16_nt (output projection)"}
+    roofline = {"bound": "mfma", "kernel": names[dom], "achieved": kernel_tflops[dom], "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": kernel_tflops[dom] / PEAK_F16_TFLOPS, "traffic": None,
+                "flops_per_launch": fl[dom], "avg_launch_ms": kern[dom]["mean"]}
+    log(f"  {ms:.3f} ms/forward; kernels ms: " + ", ".join(f"{n} {kern[n]['mean']:.3f}" for n in fl))
+
+    extra = []
+    if not args.quick:
+        w, st = max(1, args.warmup // 2), max(3, args.steps // 4)
+        for s2, h2, nh2 in ((16384, 4096, 32), (32768, 4096, 32), (65536, 4096, 32), (8192, 8192, 64)):
+            log(f"block seq {s2} hidden {h2}")
+            m2, k2 = run_block(torch, B, hip, s2, h2, nh2, 1, w, st)
+            f2 = block_flops(s2, h2)
+            extra.append({"workload": f"block forward seq {s2} hidden {h2} heads {nh2} fp16", "ms_per_forward": m2,
+                          "attention_ms": k2["attn"]["mean"],
+                          "attention_tflops": f2["attn"] / (k2["attn"]["mean"] * 1e-3) / 1e12,
+                          "attention_frac_of_peak": f2["attn"] / (k2["attn"]["mean"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                          "qkv_tflops": f2["qkv"] / (k2["qkv"]["mean"] * 1e-3) / 1e12,
+                          "oproj_tflops": f2["oproj"] / (k2["oproj"]["mean"] * 1e-3) / 1e12,
+                          "block_tflops": sum(f2.values()) / (m2 * 1e-3) / 1e12})
+            log(f"  {m2:.3f} ms/forward, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s")
+        log("rank share")
+        extra.append(run_rank_share(torch, B, hip, w, st))
+        log(f"  {extra[-1]['ms']:.3f} ms, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s, merge "
+            f"{extra[-1]['merge_gbs']:.0f} GB/s")
+        log("6 stacked blocks seq 32768")
+        m6, k6 = run_block(torch, B, hip, 32768, 4096, 32, 6, 1, 3)
+        f6 = block_flops(32768, 4096)
+        extra.append({"workload": "6 stacked blocks seq 32768 hidden 4096 heads 32 fp16", "ms_per_forward": m6,
+                      "block_tflops": 6 * sum(f6.values()) / (m6 * 1e-3) / 1e12,
+                      "attention_tflops": f6["attn"] / (k6["attn"]["mean"] * 1e-3) / 1e12})
+        log(f"  {m6:.3f} ms per 6-block forward")
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (fp64 oracle, bounded sample)")
+        cpu = cpu_baseline()
+        log(f"  {cpu['seconds']:.1f} s, {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": total_flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "self-attention block forward, non-causal: QKV projection + q_scaled + "
+                               "attention + output projection", "seq_len": seq, "batch": 1, "hidden": h,
+                   "heads": nh, "head_dim": h // nh, "dtype": "fp16", "seed": 0},
+        "ms_per_forward": kern["step"],
+        "attention": {"ms": kern["attn"]["mean"], "tflops": kernel_tflops["attn"],
+                      "frac_of_peak": kernel_tflops["attn"] / PEAK_F16_TFLOPS},
+        "kernels_ms": {n: kern[n] for n in ("qkv", "attn", "oproj")},
+        "kernels_tflops": kernel_tflops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+        "context_b200": B200_CONTEXT,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -84,6 +84,10 @@ typedef struct attn_block attn_block_t;
  *   qkv_only  non-zero: stop after the QKV projection (q_scaled, k, v_t are
  *             written; attention and the output projection are skipped and
  *             y is not written). This is how the rank share gets its inputs.
+ *   events    NULL, or 4 caller-created hipEvent_t recorded on `stream`
+ *             before the QKV projection, after it, after attention and after
+ *             the output projection (kernel timing in the real launch
+ *             configuration). With qkv_only only the first two are recorded.
  */
 typedef struct {
     void *q_scaled;
@@ -92,6 +96,7 @@ typedef struct {
     void *attn_out;
     float *lse;
     int qkv_only;
+    hipEvent_t *events;
 } attn_taps_t;
 
 /*

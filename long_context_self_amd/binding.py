@@ -43,7 +43,8 @@ class AttnError(RuntimeError):
 
 class Taps(ctypes.Structure):
     _fields_ = [("q_scaled", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v_t", ctypes.c_void_p),
-                ("attn_out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("qkv_only", ctypes.c_int)]
+                ("attn_out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("qkv_only", ctypes.c_int),
+                ("events", ctypes.c_void_p)]
 
 
 _lib = None

@@ -138,7 +138,8 @@ ATTN_API void attn_block_destroy(attn_block_t *blk) {
 ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int64_t seq, int64_t batch,
                                           const attn_taps_t *taps, hipStream_t stream) {
     TapsView tv{};
-    if (taps) tv = TapsView{taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->lse, taps->qkv_only};
+    if (taps)
+        tv = TapsView{taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->lse, taps->qkv_only, taps->events};
     Check c = validate_forward(blk == nullptr, blk ? blk->dt : 0, blk ? blk->hidden : 0,
                                blk ? blk->max_tokens : 0, x, y, seq, batch, taps ? &tv : nullptr);
     if (c.status != kOk) return report(c);
@@ -153,6 +154,10 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
     void *o = (taps && taps->attn_out) ? taps->attn_out : blk->ws_o;
     float *lse = taps ? taps->lse : nullptr;
     const bool qkv_only = taps && taps->qkv_only;
+    hipEvent_t *ev = taps ? taps->events : nullptr;
+#define MARK(i) \
+    if (ev) HIP_TRY("attn_block_forward: hipEventRecord", hipEventRecord(ev[i], stream))
+    MARK(0);
 
     if (blk->dt == kF16) {
         GemmArgs g{};
@@ -172,6 +177,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.head_dim = d;
         g.q_scale = q_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f16(g, stream));
+        MARK(1);
         if (qkv_only) return ATTN_OK;
         FlashArgs fa{};
         fa.q = g.q;
@@ -188,6 +194,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         fa.o16_ld = h;
         fa.lse = lse;
         HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
+        MARK(2);
         GemmArgs go{};
         go.a = static_cast<const _Float16 *>(o);
         go.lda = h;
@@ -200,6 +207,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         go.c = static_cast<_Float16 *>(y);
         go.ldc = h;
         HIP_TRY("attn_block_forward: output projection", launch_gemm_f16(go, stream));
+        MARK(3);
     } else {
         GemmArgsF32 g{};
         g.a = static_cast<const float *>(x);
@@ -218,6 +226,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.head_dim = d;
         g.q_scale = q_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f32(g, stream));
+        MARK(1);
         if (qkv_only) return ATTN_OK;
         FlashArgsF32 fa{};
         fa.q = g.q;
@@ -235,6 +244,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         fa.otok_ld = h;
         fa.lse = lse;
         HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f32(fa, stream));
+        MARK(2);
         GemmArgsF32 go{};
         go.a = static_cast<const float *>(o);
         go.lda = h;
@@ -247,7 +257,9 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         go.c = static_cast<float *>(y);
         go.ldc = h;
         HIP_TRY("attn_block_forward: output projection", launch_gemm_f32(go, stream));
+        MARK(3);
     }
+#undef MARK
     return ATTN_OK;
 }
 

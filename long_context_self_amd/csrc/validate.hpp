@@ -77,6 +77,7 @@ struct TapsView {
     const void *q_scaled, *k, *v_t, *attn_out;
     const float *lse;
     int qkv_only;
+    const void *events;  // array of 4 events; entries are checked by the caller
 };
 
 inline Check validate_forward(bool blk_null, int dt, int hidden, int64_t max_tokens, const void *x,
