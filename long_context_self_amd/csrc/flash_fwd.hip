@@ -13,8 +13,16 @@
 //
 // Design (MI355X):
 // * One workgroup = 256 query rows of one head, 8 waves (2 per SIMD), 32 rows
-//   per wave. K and V^T tiles of 64 keys are double-buffered in LDS (32 KiB
-//   per stage) with XOR swizzles that make every ds_read_b128 conflict-free.
+//   per wave. K and V^T tiles of 64 keys are double-buffered in LDS with
+//   padded pitches that keep every ds_read_b128 conflict-free and every
+//   fragment address a base register plus an immediate offset. Both waves of
+//   a SIMD read LDS concurrently: on gfx950 one wave per SIMD sustains only
+//   about half the LDS read bandwidth that two do.
+// * Each wave's tile step issues the MFMAs of S_j = K_j Q^T together with
+//   those of O += V_{j-1} P_{j-1} (independent, so they interleave), with the
+//   LDS fragment reads pipelined four MFMAs ahead, then the softmax of S_j.
+//   One barrier per tile; between barriers the two waves of a SIMD drift, so
+//   one's softmax overlaps the other's MFMAs.
 // * S^T = K Q^T on v_mfma_f32_32x32x16_f16 with Q held in registers as the B
 //   operand. K rows are read in a permuted order so that each lane's
 //   accumulator holds 16 consecutive keys of its own query; those fp32 scores
@@ -40,88 +48,96 @@ constexpr int BQ = 256;         // query rows per workgroup
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int BN = 64;          // keys per tile
-constexpr int K_TILE = BN * D;  // halves
-constexpr int V_TILE = D * BN;  // halves
+// LDS layouts (padded pitches, so every fragment read is one base register
+// plus a compile-time offset):
+// * K tile: 64 key rows of 128 halves at a pitch of 136 halves (272 B). Key k
+//   is stored in row ksig(k) (bits 3 and 4 of k swapped): the 16 lanes of one
+//   LDS pass then read 16 rows that are distinct mod 16, and with a pitch of
+//   17 16-byte units their chunks fall in 16 distinct bank groups.
+// * V^T tile: 128 rows (head dims) of 64 keys at a pitch of 72 halves (144 B):
+//   16 consecutive rows at pitch 9 units are also 16 distinct bank groups.
+constexpr int KP = D + 8;                     // K pitch (halves)
+constexpr int VP = BN + 8;                    // V^T pitch (halves)
+constexpr int K_TILE = BN * KP;               // halves
+constexpr int V_TILE = D * VP;                // halves
 constexpr float kRescaleTau = 8.0f * kLn2;  // rescale only when a max grows by > 2^8
 
-// Swizzled 16-byte chunk index inside a K row (16 chunks of 8 halves).
-__device__ __forceinline__ int swz_k(int row) { return (row & 7) | (((row >> 4) & 1) << 3); }
-// Swizzled chunk inside a V^T row (8 chunks of 8 keys).
-__device__ __forceinline__ int swz_v(int d) { return (d >> 1) & 7; }
+__device__ __forceinline__ int ksig(int k) { return (k & ~24) | ((k & 8) << 1) | ((k & 16) >> 1); }
 // Accumulator row i of a 32x32 S^T block holds key perm_key(i): lane half h
 // then owns keys 16h..16h+15 in accumulator order.
 __device__ __forceinline__ int perm_key(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-struct Stage {
-    u32x4 k[2];
-    u32x4 v[2];
-};
-
-// Global -> registers for the tile starting at key0. K rows past skv are
-// clamped to the last key (finite values; their scores are masked). V^T keys
-// past skv are zero so that masked probabilities multiply zeros.
-__device__ __forceinline__ void load_tile(Stage &st, const FlashArgs &a, const half_t *kh,
-                                          const half_t *vh, int key0, int tid) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int row = i >> 4, c = i & 15;
-        int key = min(key0 + row, a.skv - 1);
-        st.k[p] = ldg16(kh + (int64_t)key * D + c * 8);
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int d = i >> 3, c = i & 7;
-        int kstart = key0 + c * 8;
-        const half_t *src = vh + (int64_t)d * a.v_row_stride + kstart;
-        if (kstart + 8 <= a.skv) {
-            st.v[p] = ldg16(src);
-        } else {
-            half8 t;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = (kstart + e < a.skv) ? src[e] : (half_t)0.0f;
-            st.v[p] = as_u32x4(t);
-        }
-    }
-}
-
-__device__ __forceinline__ void store_tile(const Stage &st, half_t *ks, half_t *vs, int tid) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int row = i >> 4, c = i & 15;
-        *reinterpret_cast<u32x4 *>(ks + row * D + ((c ^ swz_k(row)) << 3)) = st.k[p];
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int d = i >> 3, c = i & 7;
-        *reinterpret_cast<u32x4 *>(vs + d * BN + ((c ^ swz_v(d)) << 3)) = st.v[p];
-    }
-}
-
-template <bool MASK>
-__device__ __forceinline__ void tile_step(const half_t *ks, const half_t *vs, const half8 (&qf)[8],
-                                          floatx16 (&o)[4], float &m_run, float &l_run, int lane,
-                                          int key0, int skv) {
+// ---- M phase: S_j = K_j Q^T (if HAS_G1) and O^T += V_{j-1}^T P_{j-1}^T (if HAS_G2).
+// The products are independent, so their MFMAs interleave. Operand fragments
+// come from LDS through a double buffer of four: the reads for MFMAs n+4..n+7
+// are in flight while MFMAs n..n+3 execute.
+template <bool HAS_G1, bool HAS_G2>
+__device__ __forceinline__ void mfma_phase(const half_t *ks, const half_t *vs, const half8 (&qf)[8],
+                                           const half8 (&pf)[2][2], floatx16 (&s)[2], floatx16 (&o)[4],
+                                           int lane) {
     const int h = lane >> 5;
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks) x 32 queries
-    floatx16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = floatx16{};
-        const int row = 32 * kb + perm_key(lane & 31);
-        const half_t *krow = ks + row * D;
-        const int sw = swz_k(row);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int c = 2 * kk + h;
-            half8 a = *reinterpret_cast<const half8 *>(krow + ((c ^ sw) << 3));
-            s[kb] = mfma32(a, qf[kk], s[kb]);
+    const half_t *kbase = ks + ksig(perm_key(lane & 31)) * KP + 8 * h;
+    const half_t *vbase = vs + (lane & 31) * VP + 16 * h;
+    constexpr int N = (HAS_G1 ? 16 : 0) + (HAS_G2 ? 16 : 0);
+    // MFMA n of this phase: kind 0 = S block kb at k-step i; kind 1 = O block
+    // mb with key block kb and half t.
+    auto decode = [](int n, int &kind, int &i, int &kb, int &mb, int &t) {
+        if (HAS_G1 && HAS_G2) {
+            const int u = n & 3, step = n >> 2;
+            kind = u >> 1;
+            if (kind == 0) {
+                i = step;
+                kb = u & 1;
+            } else {
+                const int g = 2 * step + (u & 1);
+                mb = g >> 2;
+                kb = (g >> 1) & 1;
+                t = g & 1;
+            }
+        } else if (HAS_G1) {
+            kind = 0;
+            i = n >> 1;
+            kb = n & 1;
+        } else {
+            kind = 1;
+            mb = n >> 2;
+            kb = (n >> 1) & 1;
+            t = n & 1;
         }
+    };
+    auto frag = [&](int n) -> half8 {
+        int kind = 0, i = 0, kb = 0, mb = 0, t = 0;
+        decode(n, kind, i, kb, mb, t);
+        if (kind == 0) return *reinterpret_cast<const half8 *>(kbase + kb * 32 * KP + 16 * i);
+        return *reinterpret_cast<const half8 *>(vbase + 32 * mb * VP + 32 * kb + 8 * t);
+    };
+    auto mma = [&](int n, const half8 &a) {
+        int kind = 0, i = 0, kb = 0, mb = 0, t = 0;
+        decode(n, kind, i, kb, mb, t);
+        if (kind == 0)
+            s[kb] = (i == 0) ? mfma32(a, qf[i], floatx16{}) : mfma32(a, qf[i], s[kb]);
+        else
+            o[mb] = mfma32(a, pf[kb][t], o[mb]);
+    };
+    half8 buf[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buf[0][j] = frag(j);
+#pragma unroll
+    for (int step = 0; step < N / 4; ++step) {
+        if (step + 1 < N / 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) buf[(step + 1) & 1][j] = frag(4 * (step + 1) + j);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma(4 * step + j, buf[step & 1][j]);
     }
-    // ---- mask keys past the end (last tile only)
+}
+
+// ---- S phase: online softmax of S_j -> P_j (fp16), running max/sum, lazy O rescale.
+template <bool MASK>
+__device__ __forceinline__ void softmax_phase(floatx16 (&s)[2], half8 (&pf)[2][2], floatx16 (&o)[4],
+                                              float &m_run, float &l_run, int lane, int key0, int skv) {
+    const int h = lane >> 5;
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -131,14 +147,12 @@ __device__ __forceinline__ void tile_step(const half_t *ks, const half_t *vs, co
                 if (key >= skv) s[kb][i] = -INFINITY;
             }
     }
-    // ---- row max over this tile (in-lane, then across the two lane halves)
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
     mt = wave_max_across_halves(mt);
-    // ---- lazy rescale: only when some row's max grew by more than tau
     const bool need = mt > m_run + kRescaleTau;
     if (__ballot(need)) {
         const float m_new = need ? mt : m_run;
@@ -148,9 +162,7 @@ __device__ __forceinline__ void tile_step(const half_t *ks, const half_t *vs, co
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
     }
-    // ---- p = exp(s - m), row sum, fp16 B operand of P^T
     const float mneg = -m_run * kLog2e;
-    half8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -161,28 +173,101 @@ __device__ __forceinline__ void tile_step(const half_t *ks, const half_t *vs, co
                 l_run += p;
                 pf[kb][t][j] = (half_t)p;
             }
-    // ---- O^T += V^T P^T
+}
+
+// Per-thread offsets of the 16-byte chunks a thread moves for every tile (two
+// of the K tile, 64 rows x 16 chunks; two of the V^T tile, 128 rows x 8
+// chunks). Global offsets are relative to the tile's first key, so a tile's
+// load is one scalar base plus loop-invariant offsets.
+struct TileOffsets {
+    int kg[2], kl[2], vg[2], vl[2], krow[2], vkey[2];
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(const FlashArgs &a, int tid) {
+    TileOffsets t;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int d = 32 * mb + (lane & 31);
-        const half_t *vrow = vs + d * BN;
-        const int sw = swz_v(d);
+    for (int p = 0; p < 2; ++p) {
+        const int i = tid + NTHREADS * p;
+        const int row = i >> 4, c = i & 15;
+        t.krow[p] = row;
+        t.kg[p] = row * D + c * 8;
+        t.kl[p] = ksig(row) * KP + c * 8;
+        const int d = i >> 3, cv = i & 7;
+        t.vkey[p] = cv * 8;
+        t.vg[p] = d * (int)a.v_row_stride + cv * 8;
+        t.vl[p] = d * VP + cv * 8;
+    }
+    return t;
+}
+
+// K tile starting at key0 -> registers. Rows past skv are clamped to the last
+// key (finite values; their scores are masked).
+__device__ __forceinline__ void load_k(u32x4 (&st)[2], const FlashArgs &a, const half_t *kh, int key0,
+                                       const TileOffsets &t) {
+    if (key0 + BN <= a.skv) {
+        const half_t *kt = kh + (int64_t)key0 * D;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int p = 0; p < 2; ++p) st[p] = ldg16(kt + t.kg[p]);
+    } else {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int c = 4 * kb + 2 * h + t;
-                half8 a = *reinterpret_cast<const half8 *>(vrow + ((c ^ sw) << 3));
-                o[mb] = mfma32(a, pf[kb][t], o[mb]);
-            }
+        for (int p = 0; p < 2; ++p) {
+            const int key = min(key0 + t.krow[p], a.skv - 1);
+            st[p] = ldg16(kh + (int64_t)key * D + (t.kg[p] - t.krow[p] * D));
+        }
     }
 }
 
+// V^T tile starting at key0 -> registers; keys past skv are zero so that the
+// masked probabilities multiply zeros.
+__device__ __forceinline__ void load_v(u32x4 (&st)[2], const FlashArgs &a, const half_t *vh, int key0,
+                                       const TileOffsets &t) {
+    const half_t *vt = vh + key0;
+    if (key0 + BN <= a.skv) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) st[p] = ldg16(vt + t.vg[p]);
+    } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int kstart = key0 + t.vkey[p];
+            const half_t *src = vt + t.vg[p];
+            half8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (kstart + e < a.skv) ? src[e] : (half_t)0.0f;
+            st[p] = as_u32x4(v);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_k(const u32x4 (&st)[2], half_t *ks, const TileOffsets &t) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4 *>(ks + t.kl[p]) = st[p];
+}
+
+__device__ __forceinline__ void store_v(const u32x4 (&st)[2], half_t *vs, const TileOffsets &t) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4 *>(vs + t.vl[p]) = st[p];
+}
+
+__device__ __forceinline__ void softmax_tile(floatx16 (&s)[2], half8 (&pf)[2][2], floatx16 (&o)[4],
+                                             float &m_run, float &l_run, int lane, int j, int skv) {
+    if ((j + 1) * BN <= skv)
+        softmax_phase<false>(s, pf, o, m_run, l_run, lane, j * BN, skv);
+    else
+        softmax_phase<true>(s, pf, o, m_run, l_run, lane, j * BN, skv);
+}
+
+// Tile j holds K_j in ksm[j % 2] and V_j in vsm[j % 2]. Step j computes
+// S_j = K_j Q^T and O += V_{j-1} P_{j-1}, then the softmax of S_j; meanwhile
+// K_{j+1} and V_j are loaded into registers and stored at the end of the step
+// into ksm[(j+1) % 2] and vsm[j % 2]. Both buffers were last read in step j-1,
+// which every wave finished before the barrier that ended it; the barrier at
+// the end of step j publishes them. A final step adds V_{T-1} P_{T-1}.
 __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
-    __shared__ __attribute__((aligned(16))) half_t smem[2 * (K_TILE + V_TILE)];
+    __shared__ __attribute__((aligned(16))) half_t ksm[2 * K_TILE];
+    __shared__ __attribute__((aligned(16))) half_t vsm[2 * V_TILE];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int h = lane >> 5;
 
     const int nqb = (a.sq + BQ - 1) / BQ;
@@ -194,40 +279,60 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     const half_t *kh = a.k + (int64_t)head * a.k_head_stride;
     const half_t *vh = a.vt + (int64_t)head * a.v_head_stride;
 
-    // Q rows of this lane (clamped past the end), as 8 B-operand fragments.
     const int q = qb * BQ + wave * 32 + (lane & 31);
     const int qc = min(q, a.sq - 1);
     half8 qf[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 16 + 8 * h));
 
-    floatx16 o[4];
+    floatx16 o[4], s[2];
+    half8 pf[2][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) o[mb] = floatx16{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int ntiles = (a.skv + BN - 1) / BN;
-    const int nfull = a.skv / BN;
-    Stage st;
-    if (ntiles > 0) {
-        load_tile(st, a, kh, vh, 0, tid);
-        store_tile(st, smem, smem + K_TILE, tid);
-    }
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        half_t *ks = smem + (j & 1) * (K_TILE + V_TILE);
-        half_t *vs = ks + K_TILE;
-        const bool more = j + 1 < ntiles;
-        if (more) load_tile(st, a, kh, vh, (j + 1) * BN, tid);
-        if (j < nfull)
-            tile_step<false>(ks, vs, qf, o, m_run, l_run, lane, j * BN, a.skv);
-        else
-            tile_step<true>(ks, vs, qf, o, m_run, l_run, lane, j * BN, a.skv);
-        if (more) {
-            half_t *ks2 = smem + ((j + 1) & 1) * (K_TILE + V_TILE);
-            store_tile(st, ks2, ks2 + K_TILE, tid);
-        }
+    const int T = (a.skv + BN - 1) / BN;
+    if (T > 0) {
+        const TileOffsets toff = tile_offsets(a, tid);
+        u32x4 sk[2], sv[2];
+        load_k(sk, a, kh, 0, toff);
+        store_k(sk, ksm, toff);
         __syncthreads();
+        // step 0: S_0 only
+        if (T > 1) load_k(sk, a, kh, BN, toff);
+        load_v(sv, a, vh, 0, toff);
+        mfma_phase<true, false>(ksm, vsm, qf, pf, s, o, lane);
+        softmax_tile(s, pf, o, m_run, l_run, lane, 0, a.skv);
+        if (T > 1) store_k(sk, ksm + K_TILE, toff);
+        store_v(sv, vsm, toff);
+        __syncthreads();
+        // Steady state: K_{j+1} and V_j are full tiles and S_j needs no mask,
+        // so the loads are branch-free and stay in flight across the MFMAs.
+        int j = 1;
+        for (; j + 2 < T; ++j) {
+            const half_t *kt = kh + (int64_t)(j + 1) * BN * D;
+            const half_t *vt = vh + j * BN;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) sk[p] = ldg16(kt + toff.kg[p]);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) sv[p] = ldg16(vt + toff.vg[p]);
+            mfma_phase<true, true>(ksm + (j & 1) * K_TILE, vsm + ((j - 1) & 1) * V_TILE, qf, pf, s, o, lane);
+            softmax_phase<false>(s, pf, o, m_run, l_run, lane, j * BN, a.skv);
+            store_k(sk, ksm + ((j + 1) & 1) * K_TILE, toff);
+            store_v(sv, vsm + (j & 1) * V_TILE, toff);
+            __syncthreads();
+        }
+        // The last (at most two) steps, whose loads may touch the partial tile.
+        for (; j < T; ++j) {
+            if (j + 1 < T) load_k(sk, a, kh, (j + 1) * BN, toff);
+            load_v(sv, a, vh, j * BN, toff);
+            mfma_phase<true, true>(ksm + (j & 1) * K_TILE, vsm + ((j - 1) & 1) * V_TILE, qf, pf, s, o, lane);
+            softmax_tile(s, pf, o, m_run, l_run, lane, j, a.skv);
+            if (j + 1 < T) store_k(sk, ksm + ((j + 1) & 1) * K_TILE, toff);
+            store_v(sv, vsm + (j & 1) * V_TILE, toff);
+            __syncthreads();
+        }
+        mfma_phase<false, true>(ksm, vsm + ((T - 1) & 1) * V_TILE, qf, pf, s, o, lane);
     }
 
     if (q >= a.sq) return;
@@ -243,7 +348,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
             for (int g = 0; g < 4; ++g) {
                 floatx4 v;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = o[mb][4 * g + r] * inv;
+                for (int rr = 0; rr < 4; ++rr) v[rr] = o[mb][4 * g + rr] * inv;
                 *reinterpret_cast<floatx4 *>(dst + 32 * mb + 8 * g + 4 * h) = v;
             }
     }
@@ -255,7 +360,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
             for (int g = 0; g < 4; ++g) {
                 half4 v;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = (half_t)(o[mb][4 * g + r] * inv);
+                for (int rr = 0; rr < 4; ++rr) v[rr] = (half_t)(o[mb][4 * g + rr] * inv);
                 *reinterpret_cast<half4 *>(dst + 32 * mb + 8 * g + 4 * h) = v;
             }
     }
