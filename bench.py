@@ -207,10 +207,10 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
     }
 
 
-def cpu_baseline(seq=8192, h=4096, nh=32, rows=2048, seed=0):
+def cpu_baseline(seq=8192, h=4096, nh=32, rows=8192, seed=0):
     """The fp64 oracle on a bounded sample of the headline workload: K and V
-    over all seq rows, and rows `rows` sampled query rows through attention and
-    the output projection (exact for those rows)."""
+    over all seq rows, and `rows` sampled query rows (all of them by default)
+    through attention and the output projection (exact for those rows)."""
     import oracle
     from long_context_self_amd.synthetic import block_inputs, sample_rows
 
@@ -228,9 +228,30 @@ def cpu_baseline(seq=8192, h=4096, nh=32, rows=2048, seed=0):
     flops = 4.0 * seq * h * h + len(r) * (2.0 * h * h + 4.0 * seq * h + 2.0 * h * h)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": dt,
-            "sample": f"fp64 numpy oracle, seq {seq} hidden {h} 32 heads: K and V over all {seq} rows plus "
-                      f"{len(r)} sampled query rows through attention and W_O; value = algorithmic FLOPs of "
-                      f"that work / wall time"}
+            "sample": f"fp64 numpy oracle, seq {seq} hidden {h} 32 heads: K and V over all {seq} rows and "
+                      f"{len(r)} query rows through attention and W_O (one full block forward when all rows); "
+                      f"value = algorithmic FLOPs of that work / wall time"}
+
+
+def trace_summary(path: str) -> str:
+    """Per (kernel, grid size) dispatch count and mean/min/max duration from a
+    rocprofv3 --kernel-trace CSV, as a markdown table."""
+    import csv
+    import collections
+
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            short = name.replace("attnblk::(anonymous namespace)::", "").split("(")[0]
+            key = (short, int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1),
+                   int(r["Workgroup_Size_X"]))
+            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    lines = ["| kernel | grid threads | workgroup | dispatches | mean ms | min ms | max ms |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, g, w), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {g} | {w} | {len(v)} | {np.mean(v):.4f} | {np.min(v):.4f} | {np.max(v):.4f} |")
+    return "\n".join(lines)
 
 
 def main() -> int:
@@ -242,7 +263,12 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print a per-(kernel, grid) summary of a rocprofv3 kernel-trace CSV and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library builds no "
               f"multi-GPU path)", file=sys.stderr)
