@@ -10,9 +10,10 @@
 // "What is hint.json?".
 //
 // Design (MI355X): 256x256 tile per workgroup, 8 waves (2 per SIMD) of
-// 128x64 each on v_mfma_f32_32x32x16_f16, K in steps of 32 double-buffered
-// through LDS with an XOR swizzle (conflict-free ds_read_b128), global loads
-// for step k+1 in flight during the MFMAs of step k. Tiles are grouped 4 deep
+// 128x64 each on v_mfma_f32_32x32x16_f16. K advances in steps of 32 through a
+// four-stage LDS ring filled by direct global->LDS loads (no staging
+// registers), issued three steps ahead; one barrier per step. An XOR swizzle
+// applied on the load side makes every ds_read_b128 conflict-free. Tiles are grouped 4 deep
 // in M and each XCD gets a contiguous range of tiles so its L2 holds the A
 // and B panels its workgroups share. The epilogue stages the fp16 tile in
 // LDS (transposed for V) and writes 16-byte chunks.
@@ -26,51 +27,72 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NTHREADS = 512;
+constexpr int STAGES = 4;
 constexpr int GROUP_M = 4;
 constexpr int A_TILE = BM * BK;  // halves
 constexpr int B_TILE = BN * BK;
+constexpr int STAGE = A_TILE + B_TILE;
 constexpr int CP = BN + 8;       // epilogue pitch (halves)
-constexpr int SMEM_MAIN = 2 * (A_TILE + B_TILE) * 2;  // bytes
+constexpr int SMEM_MAIN = STAGES * STAGE * 2;  // bytes
 constexpr int SMEM_EPI = BM * CP * 2;
 constexpr int SMEM_BYTES = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
 
-// 64-byte rows of 4 chunks; chunk c of row r lives at c ^ ((r >> 2) & 3).
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// LDS tile layout: 64-byte rows of four 16-byte chunks; logical chunk c of
+// row r sits at physical chunk c ^ swz(r), which spreads the 16 rows one LDS
+// pass reads over all 16 bank groups. swz depends only on bits 2-3 of the
+// row, which are the same for the four row blocks (32 rows apart) a wave
+// reads, so a fragment address is one base register plus an immediate.
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-struct Stage {
-    u32x4 a[2];
-    u32x4 b[2];
-};
+// s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
+// unconstrained (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
+// lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+constexpr int vmcnt_only(int n) { return (n & 0xF) | 0x70 | 0xF00 | ((n >> 4) << 14); }
 
-__device__ __forceinline__ void load_stage(Stage &st, const GemmArgs &g, int m0, int n0, int k0, int tid) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int row = i >> 2, c = i & 3;
-        int m = min(m0 + row, g.M - 1);
-        st.a[p] = ldg16(g.a + (int64_t)m * g.lda + k0 + c * 8);
-        int n = min(n0 + row, g.N - 1);
-        st.b[p] = ldg16(g.b + (int64_t)n * g.ldb + k0 + c * 8);
-    }
-}
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// would wait for every in-flight global->LDS load (they count as LDS stores),
+// emptying the prefetch ring at each step. Visibility of a stage comes from
+// each wave's explicit vmcnt wait before the barrier; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void store_stage(const Stage &st, half_t *as, half_t *bs, int tid) {
+// Issue the direct global->LDS loads of one K-step (A rows and B rows) into
+// stage buffer `st`. A global_load_lds_dwordx4 writes 64 lanes x 16 bytes to
+// consecutive LDS addresses, so each lane fetches the global chunk that its
+// LDS slot must hold. Waves 0-3 move A (16 instructions), waves 4-7 move B.
+// Interior tiles use one loop-invariant lane offset; edge tiles clamp rows
+// past M or N to the last valid row.
+template <bool EDGE>
+__device__ __forceinline__ void issue_stage(const GemmArgs &g, half_t *st, int m0, int n0, int k0, int wave,
+                                            int lane) {
+    const bool is_a = wave < 4;
+    const int w4 = wave & 3;
+    const half_t *base = is_a ? g.a : g.b;
+    const int64_t ld = is_a ? g.lda : g.ldb;
+    const int r0 = is_a ? m0 : n0;
+    const int rmax = (is_a ? g.M : g.N) - 1;
+    half_t *tile = st + (is_a ? 0 : A_TILE);
+    const int lrow = lane >> 2;                  // row within a 16-row instruction block
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk for this LDS slot
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        int i = tid + NTHREADS * p;
-        int row = i >> 2, c = i & 3;
-        int off = row * BK + ((c ^ swz(row)) << 3);
-        *reinterpret_cast<u32x4 *>(as + off) = st.a[p];
-        *reinterpret_cast<u32x4 *>(bs + off) = st.b[p];
+    for (int i = 0; i < 4; ++i) {
+        const int n = 4 * w4 + i;                // instruction index 0..15: rows 16n..16n+15
+        int row = r0 + 16 * n + lrow;
+        if (EDGE) row = min(row, rmax);
+        const half_t *src = base + (int64_t)row * ld + k0 + chunk * 8;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(tile + n * 512), 16, 0, 0);
     }
 }
 
 __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char smem_raw[SMEM_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM_BYTES];
     half_t *smem = reinterpret_cast<half_t *>(smem_raw);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int wm = wave >> 2;  // 0..1 -> rows wm*128
     const int wn = wave & 3;   // 0..3 -> cols wn*64
@@ -86,6 +108,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     const int tm = first_m + (w % per_group) % gsize;
     const int tn = (w % per_group) / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
+    const bool edge = (m0 + BM > g.M) || (n0 + BN > g.N);
 
     floatx16 acc[4][2];
 #pragma unroll
@@ -94,40 +117,78 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
         for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
     const int nk = g.K / BK;
-    Stage st;
-    load_stage(st, g, m0, n0, 0, tid);
-    store_stage(st, smem, smem + A_TILE, tid);
-    __syncthreads();
+    // prologue: stages 0..STAGES-2 in flight
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) {
+            if (edge)
+                issue_stage<true>(g, smem + s * STAGE, m0, n0, s * BK, wave, lane);
+            else
+                issue_stage<false>(g, smem + s * STAGE, m0, n0, s * BK, wave, lane);
+        }
+
+    // fragment bases: row (lane & 31) of each 32-row block, physical chunk for k-substep kk
+    const int sw = swz(lane & 31);
+    const int a_off0 = (wm * 128 + (lane & 31)) * BK + (((0 + h) ^ sw) << 3);
+    const int a_off1 = (wm * 128 + (lane & 31)) * BK + (((2 + h) ^ sw) << 3);
+    const int b_off0 = A_TILE + (wn * 64 + (lane & 31)) * BK + (((0 + h) ^ sw) << 3);
+    const int b_off1 = A_TILE + (wn * 64 + (lane & 31)) * BK + (((2 + h) ^ sw) << 3);
+
+    // Software pipeline over K substeps of 16: the fragment reads of substep
+    // t+1 are issued before the MFMAs of substep t. Barrier B_kt sits between
+    // the two substeps of step kt: every wave has then finished reading step
+    // kt-1 (its fragments fed MFMAs before B_kt), so its buffer can be refilled
+    // with step kt+STAGES-1; and each wave waited for its own loads of step
+    // kt+1 before B_kt, so step kt+1 is readable after it.
+    auto read_frags = [&](const half_t *stb, int kk, half8 (&af)[4], half8 (&bf)[2]) {
+        const half_t *ab = stb + (kk ? a_off1 : a_off0);
+        const half_t *bb = stb + (kk ? b_off1 : b_off0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const half8 *>(ab + i * 32 * BK);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const half8 *>(bb + j * 32 * BK);
+    };
+    auto mma = [&](const half8 (&af)[4], const half8 (&bf)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    };
+    // stage 0 readable (stages 1 and 2, 4 loads each, may stay in flight)
+    static_assert(STAGES == 4, "the waits below count 4 loads per stage and 3 stages in flight");
+    if (nk >= 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+    else if (nk == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(4));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    barrier_no_fence();
+    half8 a0[4], b0[2], a1[4], b1[2];
+    read_frags(smem, 0, a0, b0);
     for (int kt = 0; kt < nk; ++kt) {
-        const half_t *as = smem + (kt & 1) * (A_TILE + B_TILE);
-        const half_t *bs = as + A_TILE;
-        const bool more = kt + 1 < nk;
-        if (more) load_stage(st, g, m0, n0, (kt + 1) * BK, tid);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = 2 * kk + h;
-            half8 af[4], bf[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int row = wm * 128 + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const half8 *>(as + row * BK + ((c ^ swz(row)) << 3));
+        const half_t *stb = smem + (kt % STAGES) * STAGE;
+        read_frags(stb, 1, a1, b1);
+        mma(a0, b0);
+        if (kt + 1 < nk) {
+            // step kt+1 must be complete; steps up to kt+STAGES-2 may stay in flight
+            const int in_flight = min(nk - 1, kt + STAGES - 2) - (kt + 1);
+            if (in_flight >= 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(4));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            barrier_no_fence();
+            if (kt + STAGES - 1 < nk) {
+                const int sidx = (kt + STAGES - 1) % STAGES;
+                if (edge)
+                    issue_stage<true>(g, smem + sidx * STAGE, m0, n0, (kt + STAGES - 1) * BK, wave, lane);
+                else
+                    issue_stage<false>(g, smem + sidx * STAGE, m0, n0, (kt + STAGES - 1) * BK, wave, lane);
             }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                int row = wn * 64 + j * 32 + (lane & 31);
-                bf[j] = *reinterpret_cast<const half8 *>(bs + row * BK + ((c ^ swz(row)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+            read_frags(smem + ((kt + 1) % STAGES) * STAGE, 0, a0, b0);
         }
-        if (more) {
-            half_t *as2 = smem + ((kt + 1) & 1) * (A_TILE + B_TILE);
-            store_stage(st, as2, as2 + A_TILE, tid);
-        }
-        __syncthreads();
+        mma(a1, b1);
     }
+    __syncthreads();  // every wave is done with the stage buffers; reuse LDS for the epilogue
 
     // ---- epilogue: stage the fp16 tile in LDS, then 16-byte stores
     const bool v_tile = g.mode == kQkv && n0 >= 2 * g.hidden;
