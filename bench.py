@@ -207,7 +207,37 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
     }
 
 
-def cpu_baseline(seq=8192, h=4096, nh=32, rows=8192, seed=0):
+COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_counters_seq8192_h4096.txt")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_self_amd", "csrc")
+
+
+def hbm_traffic(kernel: str, sources: tuple[str, ...]):
+    """HBM bytes per launch of `kernel` at the headline workload from the
+    committed FETCH_SIZE / WRITE_SIZE counter readings, each scaled by what
+    the same counter reads for a plain device copy of known size; None when
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    try:
+        vals = {}
+        with open(COUNTERS) as f:
+            for line in f:
+                if line.strip() and not line.startswith("#"):
+                    k, v = line.split()
+                    vals[k] = v
+        digest = "+".join(hashlib.sha256(open(os.path.join(CSRC, s), "rb").read()).hexdigest() for s in sources)
+        if vals.get(f"{kernel}.kernel_source_sha256") != digest:
+            return None
+        cb = float(vals["copy_bytes"])
+        f_fetch = cb / (float(vals["copy_fetch_size_kib"]) * 1024)
+        f_write = cb / (float(vals["copy_write_size_kib"]) * 1024)
+        return (float(vals[f"{kernel}.fetch_size_kib"]) * 1024 * f_fetch
+                + float(vals[f"{kernel}.write_size_kib"]) * 1024 * f_write)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(seq=8192, h=4096, nh=32, rows=8192, seed=0, min_seconds=10.0, max_reps=4):
     """The fp64 oracle on a bounded sample of the headline workload: K and V
     over all seq rows, and `rows` sampled query rows (all of them by default)
     through attention and the output projection (exact for those rows)."""
@@ -222,15 +252,17 @@ def cpu_baseline(seq=8192, h=4096, nh=32, rows=8192, seed=0):
         cores = None
     x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
     r = sample_rows(seq, rows, seed=seed)
-    t0 = time.perf_counter()
-    oracle.block_forward(x, *ws, nh, rows=r)
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.block_forward(x, *ws, nh, rows=r)
+        reps += 1
     dt = time.perf_counter() - t0
-    flops = 4.0 * seq * h * h + len(r) * (2.0 * h * h + 4.0 * seq * h + 2.0 * h * h)
+    flops = reps * (4.0 * seq * h * h + len(r) * (2.0 * h * h + 4.0 * seq * h + 2.0 * h * h))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"fp64 numpy oracle, seq {seq} hidden {h} 32 heads: K and V over all {seq} rows and "
-                      f"{len(r)} query rows through attention and W_O (one full block forward when all rows); "
-                      f"value = algorithmic FLOPs of that work / wall time"}
+            "seconds": dt, "repetitions": reps,
+            "sample": f"fp64 numpy oracle, seq {seq} hidden {h} {nh} heads: K and V over all {seq} rows and "
+                      f"{len(r)} query rows through attention and W_O (one full block forward when all rows), "
+                      f"repeated {reps}x to run at least {min_seconds:.0f} s; value = algorithmic FLOPs / wall time"}
 
 
 def trace_summary(path: str) -> str:
@@ -299,8 +331,12 @@ def main() -> int:
     names = {"qkv": "gemm_f16_nt (QKV projection, fused layout epilogue)",
              "attn": "flash_fwd_f16_d128 (attention)", "oproj": "gemm_f16_nt (output projection)"}
     roofline = {"bound": "mfma", "kernel": names[dom], "achieved": kernel_tflops[dom], "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": kernel_tflops[dom] / PEAK_F16_TFLOPS, "traffic": None,
-                "flops_per_launch": fl[dom], "avg_launch_ms": kern[dom]["mean"]}
+                "unit": "TFLOP/s", "frac": kernel_tflops[dom] / PEAK_F16_TFLOPS,
+                "traffic": hbm_traffic("flash_fwd_f16_d128", ("flash_fwd.hip", "common.hpp")) if dom == "attn"
+                else None,
+                "flops_per_launch": fl[dom], "avg_launch_ms": kern[dom]["mean"],
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)",
+                "algorithmic_bytes": 4 * seq * h * 2 if dom == "attn" else None}
     log(f"  {ms:.3f} ms/forward; kernels ms: " + ", ".join(f"{n} {kern[n]['mean']:.3f}" for n in fl))
 
     extra = []
