@@ -53,6 +53,25 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
 }
 
+// Address spaces of the direct global->LDS load builtin's operands.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
+// unconstrained (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
+// lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+constexpr int vmcnt_only(int n) { return (n & 0xF) | 0x70 | 0xF00 | ((n >> 4) << 14); }
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// would wait for every in-flight global->LDS load (they count as LDS stores),
+// emptying a prefetch ring at each step. Visibility of a stage comes from
+// each wave's explicit vmcnt wait before the barrier; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
+constexpr int vmcnt_lgkm0(int n) { return (n & 0xF) | 0x70 | ((n >> 4) << 14); }
+
 __device__ __forceinline__ float wave_max_across_halves(float v) {
     return fmaxf(v, __shfl_xor(v, 32));
 }

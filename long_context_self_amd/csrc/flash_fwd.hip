@@ -13,26 +13,28 @@
 //
 // Design (MI355X):
 // * One workgroup = 256 query rows of one head, 8 waves (2 per SIMD), 32 rows
-//   per wave. K and V^T tiles of 64 keys are double-buffered in LDS with
-//   padded pitches that keep every ds_read_b128 conflict-free and every
-//   fragment address a base register plus an immediate offset. Both waves of
-//   a SIMD read LDS concurrently: on gfx950 one wave per SIMD sustains only
-//   about half the LDS read bandwidth that two do.
-// * Each wave's tile step issues the MFMAs of S_j = K_j Q^T together with
-//   those of O += V_{j-1} P_{j-1} (independent, so they interleave), with the
-//   LDS fragment reads pipelined four MFMAs ahead, then the softmax of S_j.
-//   One barrier per tile; between barriers the two waves of a SIMD drift, so
-//   one's softmax overlaps the other's MFMAs.
-// * S^T = K Q^T on v_mfma_f32_32x32x16_f16 with Q held in registers as the B
-//   operand. K rows are read in a permuted order so that each lane's
-//   accumulator holds 16 consecutive keys of its own query; those fp32 scores
-//   become, after exp and a cast, the B operand of O^T = V^T P^T without any
-//   data movement between lanes. V is stored transposed (keys contiguous) so
-//   its A operand is one 16-byte LDS read.
+//   per wave; K and V^T tiles of 64 keys.
+// * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_f16, Q held in
+//   registers as the B operand of S. K rows are taken in a permuted order so
+//   that each lane's S accumulator holds 16 consecutive keys of its own query;
+//   after exp and a cast those are the B operand of the PV product, with no
+//   data movement between lanes.
+// * Software pipeline per wave: step t issues the MFMAs of S_{t+1} and of
+//   O += V_t P_t, and while they run computes exp(S_t) -> P_t (before the PV
+//   MFMAs that need it) and then the row sums of P_t and the row maxima of
+//   S_{t+1}. The VALU softmax work thus hides under the wave's own matrix work
+//   instead of alternating with it.
+// * K/V^T reach LDS by direct global->LDS loads (no staging registers) into a
+//   4-slot ring, issued three steps ahead. LDS holds every tile in MFMA
+//   operand order: fragment n of a tile is 64 lanes x 16 bytes, so every
+//   operand read is one lane-linear ds_read_b128 (conflict-free, base register
+//   plus immediate), and each load instruction gathers exactly one fragment.
+//   One barrier per step; the next step's first operands are read before it.
 // * Softmax in the exp2 domain with the running max and sum in registers; the
-//   only cross-lane step per tile is one max between the two lanes that share
-//   a query. The O rescale is skipped unless some row's max grew by more than
-//   2^8 (exact: O and the sum always share the same reference max).
+//   O rescale is skipped unless some row's max grew by more than 2^8 (exact:
+//   O and the sum always share the same reference max).
+// * O is normalised and staged through LDS so every row leaves in full
+//   16-byte chunks of whole lines.
 // * Blocks are remapped so each XCD works through a contiguous range of
 //   (head, query block) items and its concurrent workgroups share K/V in L2.
 
@@ -43,116 +45,194 @@ namespace attnblk {
 
 namespace {
 
-constexpr int D = 128;          // head_dim
-constexpr int BQ = 256;         // query rows per workgroup
+constexpr int D = 128;       // head_dim
+constexpr int BQ = 256;      // query rows per workgroup
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int BN = 64;          // keys per tile
-// LDS layouts (padded pitches, so every fragment read is one base register
-// plus a compile-time offset):
-// * K tile: 64 key rows of 128 halves at a pitch of 136 halves (272 B). Key k
-//   is stored in row ksig(k) (bits 3 and 4 of k swapped): the 16 lanes of one
-//   LDS pass then read 16 rows that are distinct mod 16, and with a pitch of
-//   17 16-byte units their chunks fall in 16 distinct bank groups.
-// * V^T tile: 128 rows (head dims) of 64 keys at a pitch of 72 halves (144 B):
-//   16 consecutive rows at pitch 9 units are also 16 distinct bank groups.
-constexpr int KP = D + 8;                     // K pitch (halves)
-constexpr int VP = BN + 8;                    // V^T pitch (halves)
-constexpr int K_TILE = BN * KP;               // halves
-constexpr int V_TILE = D * VP;                // halves
+constexpr int BN = 64;       // keys per tile
+constexpr int FRAG = 64 * 8;              // halves in one MFMA operand fragment
+constexpr int NFRAG = 16;                 // fragments per K tile and per V^T tile
+constexpr int SLOT = 2 * NFRAG * FRAG;    // halves per ring slot: K part, then V^T part
+constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
+constexpr int RA = 4;                     // operand reads in flight ahead of the MFMAs
+constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
+constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
+constexpr int OSTAGE_BYTES = NWAVES * 32 * OP32 * 4;
+constexpr int SMEM_BYTES = RING_BYTES > OSTAGE_BYTES ? RING_BYTES : OSTAGE_BYTES;
 constexpr float kRescaleTau = 8.0f * kLn2;  // rescale only when a max grows by > 2^8
 
-__device__ __forceinline__ int ksig(int k) { return (k & ~24) | ((k & 8) << 1) | ((k & 16) >> 1); }
-// Accumulator row i of a 32x32 S^T block holds key perm_key(i): lane half h
-// then owns keys 16h..16h+15 in accumulator order.
+// Accumulator row i of a 32x32 S^T block holds key perm_key(i) of its 32-key
+// block: lane half h then owns keys 16h..16h+15 in accumulator order.
 __device__ __forceinline__ int perm_key(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-// ---- M phase: S_j = K_j Q^T (if HAS_G1) and O^T += V_{j-1}^T P_{j-1}^T (if HAS_G2).
-// The products are independent, so their MFMAs interleave. Operand fragments
-// come from LDS through a double buffer of four: the reads for MFMAs n+4..n+7
-// are in flight while MFMAs n..n+3 execute.
-template <bool HAS_G1, bool HAS_G2>
-__device__ __forceinline__ void mfma_phase(const half_t *ks, const half_t *vs, const half8 (&qf)[8],
-                                           const half8 (&pf)[2][2], floatx16 (&s)[2], floatx16 (&o)[4],
-                                           int lane) {
-    const int h = lane >> 5;
-    const half_t *kbase = ks + ksig(perm_key(lane & 31)) * KP + 8 * h;
-    const half_t *vbase = vs + (lane & 31) * VP + 16 * h;
-    constexpr int N = (HAS_G1 ? 16 : 0) + (HAS_G2 ? 16 : 0);
-    // MFMA n of this phase: kind 0 = S block kb at k-step i; kind 1 = O block
-    // mb with key block kb and half t.
-    auto decode = [](int n, int &kind, int &i, int &kb, int &mb, int &t) {
-        if (HAS_G1 && HAS_G2) {
-            const int u = n & 3, step = n >> 2;
-            kind = u >> 1;
-            if (kind == 0) {
-                i = step;
-                kb = u & 1;
-            } else {
-                const int g = 2 * step + (u & 1);
-                mb = g >> 2;
-                kb = (g >> 1) & 1;
-                t = g & 1;
-            }
-        } else if (HAS_G1) {
-            kind = 0;
-            i = n >> 1;
-            kb = n & 1;
-        } else {
-            kind = 1;
-            mb = n >> 2;
-            kb = (n >> 1) & 1;
-            t = n & 1;
-        }
-    };
-    auto frag = [&](int n) -> half8 {
-        int kind = 0, i = 0, kb = 0, mb = 0, t = 0;
-        decode(n, kind, i, kb, mb, t);
-        if (kind == 0) return *reinterpret_cast<const half8 *>(kbase + kb * 32 * KP + 16 * i);
-        return *reinterpret_cast<const half8 *>(vbase + 32 * mb * VP + 32 * kb + 8 * t);
-    };
-    auto mma = [&](int n, const half8 &a) {
-        int kind = 0, i = 0, kb = 0, mb = 0, t = 0;
-        decode(n, kind, i, kb, mb, t);
-        if (kind == 0)
-            s[kb] = (i == 0) ? mfma32(a, qf[i], floatx16{}) : mfma32(a, qf[i], s[kb]);
-        else
-            o[mb] = mfma32(a, pf[kb][t], o[mb]);
-    };
-    half8 buf[2][4];
+// Stage s = {K_{s+1}, V_s}: everything step s reads. Fragment order:
+// * K fragment n (MFMA n of a step): k-step kk = n / 2 (head dims 16kk..),
+//   key block kb = n % 2. Lane l holds K[32kb + perm_key(l % 32)][16kk + 8(l / 32) + 0..7].
+// * V^T fragment n (MFMA 16 + n): head-dim block mb = n % 4, key step ks = n / 4
+//   (key block ks / 2, half ks % 2). Lane l holds
+//   V^T[32mb + l % 32][32(ks / 2) + 16(l / 32) + 8(ks % 2) + 0..7], matching the
+//   key order of the lane's P values.
+// Wave w moves K and V^T fragments 2w and 2w + 1 of every stage.
+struct LoadOffsets {
+    uint32_t k[2], v[2];  // bytes from the tile's first key
+};
+
+__device__ __forceinline__ LoadOffsets load_offsets(const FlashArgs &a, int wave, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    LoadOffsets o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) buf[0][j] = frag(j);
+    for (int e = 0; e < 2; ++e) {
+        const int n = 2 * wave + e;
+        const int kk = n >> 1, kb = n & 1;
+        o.k[e] = (uint32_t)(((kb * 32 + perm_key(r)) * D + kk * 16 + 8 * h) * 2);
+        const int mb = n & 3, ks = n >> 2;
+        o.v[e] = (uint32_t)(((int64_t)(32 * mb + r) * a.v_row_stride + 32 * (ks >> 1) + 16 * h + 8 * (ks & 1)) * 2);
+    }
+    return o;
+}
+
+struct Ctx {
+    const char *kh, *vh;  // this head's K and V^T (bytes)
+    char *ring;           // LDS ring (wave-uniform)
+    const half_t *rl;     // LDS ring + 8 * lane (this lane's operand slot)
+    LoadOffsets lo;
+    int wave, lane, skv, T;
+    int64_t vrs;
+};
+
+__device__ __forceinline__ char *slot_k(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2; }
+__device__ __forceinline__ char *slot_v(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2 + NFRAG * FRAG * 2; }
+
+// Full K tile `tile` -> K part of slot s (two direct loads per wave).
+__device__ __forceinline__ void issue_k_full(const Ctx &c, int tile, int s) {
+    const char *base = c.kh + (int64_t)tile * BN * D * 2;
+    char *dst = slot_k(c, s) + 2 * c.wave * FRAG * 2;
 #pragma unroll
-    for (int step = 0; step < N / 4; ++step) {
-        if (step + 1 < N / 4) {
+    for (int e = 0; e < 2; ++e)
+        __builtin_amdgcn_global_load_lds((gbl_void *)(base + c.lo.k[e]), (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
+}
+
+// Full V^T tile -> V part of slot s.
+__device__ __forceinline__ void issue_v_full(const Ctx &c, int tile, int s) {
+    const char *base = c.vh + (int64_t)tile * BN * 2;
+    char *dst = slot_v(c, s) + 2 * c.wave * FRAG * 2;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) buf[(step + 1) & 1][j] = frag(4 * (step + 1) + j);
-        }
+    for (int e = 0; e < 2; ++e)
+        __builtin_amdgcn_global_load_lds((gbl_void *)(base + c.lo.v[e]), (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
+}
+
+// Last, partial K tile: rows past skv are clamped to the last key (finite
+// values; their scores are masked).
+__device__ __forceinline__ void issue_k_partial(const Ctx &c, int tile, int s) {
+    const int r = c.lane & 31, h = c.lane >> 5;
+    char *dst = slot_k(c, s) + 2 * c.wave * FRAG * 2;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma(4 * step + j, buf[step & 1][j]);
+    for (int e = 0; e < 2; ++e) {
+        const int n = 2 * c.wave + e;
+        const int kk = n >> 1, kb = n & 1;
+        const int key = min(tile * BN + kb * 32 + perm_key(r), c.skv - 1);
+        const char *src = c.kh + ((int64_t)key * D + kk * 16 + 8 * h) * 2;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
     }
 }
 
-// ---- S phase: online softmax of S_j -> P_j (fp16), running max/sum, lazy O rescale.
+// Last, partial V^T tile through registers: keys past skv are stored as
+// zeros, so the zero probabilities of masked keys never meet non-finite data.
+__device__ __forceinline__ void stage_v_partial(const Ctx &c, int tile, int s) {
+    const int r = c.lane & 31, h = c.lane >> 5;
+    half_t *dst = reinterpret_cast<half_t *>(slot_v(c, s)) + 2 * c.wave * FRAG + 8 * c.lane;
+    const half_t *vh = reinterpret_cast<const half_t *>(c.vh);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int n = 2 * c.wave + e;
+        const int mb = n & 3, ks = n >> 2;
+        const int key = tile * BN + 32 * (ks >> 1) + 16 * h + 8 * (ks & 1);
+        const half_t *src = vh + (int64_t)(32 * mb + r) * c.vrs + key;
+        half8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (key + j < c.skv) ? src[j] : (half_t)0.0f;
+        *reinterpret_cast<half8 *>(dst + e * FRAG) = v;
+    }
+}
+
+// Issue stage s (any position in the key loop); returns the number of direct
+// loads it left in flight (register-path loads complete before returning).
+__device__ __forceinline__ int issue_stage(const Ctx &c, int s) {
+    int n = 0;
+    const int kt = s + 1;
+    if (kt < c.T) {
+        if ((kt + 1) * BN <= c.skv)
+            issue_k_full(c, kt, s);
+        else
+            issue_k_partial(c, kt, s);
+        n += 2;
+    }
+    if (s >= 0 && s < c.T) {
+        if ((s + 1) * BN <= c.skv) {
+            issue_v_full(c, s, s);
+            n += 2;
+        } else {
+            stage_v_partial(c, s, s);
+        }
+    }
+    return n;
+}
+
+// Wait until at most n direct loads are in flight and every LDS access of
+// this wave is complete.
+__device__ __forceinline__ void wait_vm_lgkm(int n) {
+    if (n >= 4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(4));
+    else if (n >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(2));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+}
+
+__device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<const half8 *>(p); }
+
+// exp(S - m) in place (exp2 domain) and the fp16 B operands of the PV product.
+__device__ __forceinline__ void exp_and_pack(floatx16 (&sc)[2], half8 (&pf)[4], float mneg) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kLog2e, mneg));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[ks][j] = (half_t)sc[ks >> 1][8 * (ks & 1) + j];
+}
+
+__device__ __forceinline__ float row_sum(const floatx16 (&p)[2]) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i & 3] += p[kb][i];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 template <bool MASK>
-__device__ __forceinline__ void softmax_phase(floatx16 (&s)[2], half8 (&pf)[2][2], floatx16 (&o)[4],
-                                              float &m_run, float &l_run, int lane, int key0, int skv) {
-    const int h = lane >> 5;
+__device__ __forceinline__ float row_max(floatx16 (&s)[2], int key0, int skv, int h) {
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                int key = key0 + 32 * kb + 16 * h + i;
-                if (key >= skv) s[kb][i] = -INFINITY;
-            }
+            for (int i = 0; i < 16; ++i)
+                if (key0 + 32 * kb + 16 * h + i >= skv) s[kb][i] = -INFINITY;
     }
-    float mt = s[0][0];
+    float a[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-    mt = wave_max_across_halves(mt);
+        for (int i = (kb == 0 ? 4 : 0); i < 16; ++i) a[i & 3] = fmaxf(a[i & 3], s[kb][i]);
+    return wave_max_across_halves(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+}
+
+// New row max mt of the next scores: raise the reference max where it grew by
+// more than 2^8 and rescale O and the running sum to it (skipped when no row
+// of the wave needs it).
+__device__ __forceinline__ void update_max(float mt, float &m_run, float &l_run, floatx16 (&o)[4]) {
     const bool need = mt > m_run + kRescaleTau;
     if (__ballot(need)) {
         const float m_new = need ? mt : m_run;
@@ -162,109 +242,94 @@ __device__ __forceinline__ void softmax_phase(floatx16 (&s)[2], half8 (&pf)[2][2
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
     }
-    const float mneg = -m_run * kLog2e;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j], kLog2e, mneg));
-                l_run += p;
-                pf[kb][t][j] = (half_t)p;
-            }
 }
 
-// Per-thread offsets of the 16-byte chunks a thread moves for every tile (two
-// of the K tile, 64 rows x 16 chunks; two of the V^T tile, 128 rows x 8
-// chunks). Global offsets are relative to the tile's first key, so a tile's
-// load is one scalar base plus loop-invariant offsets.
-struct TileOffsets {
-    int kg[2], kl[2], vg[2], vl[2], krow[2], vkey[2];
-};
-
-__device__ __forceinline__ TileOffsets tile_offsets(const FlashArgs &a, int tid) {
-    TileOffsets t;
+// Steady step t: every tile it touches is full, stage t+3 exists and is
+// full, and step t+1 starts with S_{t+2} MFMAs. fr holds this step's first
+// RA operands on entry and the next step's on exit.
+__device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
+                                            floatx16 (&o)[4], const half8 (&qf)[8], half8 (&fr)[RA],
+                                            float &m_run, float &l_run) {
+    issue_k_full(c, t + 4, t + 3);
+    issue_v_full(c, t + 3, t + 3);
+    const half_t *cur = c.rl + (t & 3) * SLOT;
+    const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
+    half8 pf[4];
+    exp_and_pack(sc, pf, -m_run * kLog2e);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int i = tid + NTHREADS * p;
-        const int row = i >> 4, c = i & 15;
-        t.krow[p] = row;
-        t.kg[p] = row * D + c * 8;
-        t.kl[p] = ksig(row) * KP + c * 8;
-        const int d = i >> 3, cv = i & 7;
-        t.vkey[p] = cv * 8;
-        t.vg[p] = d * (int)a.v_row_stride + cv * 8;
-        t.vl[p] = d * VP + cv * 8;
-    }
-    return t;
-}
-
-// K tile starting at key0 -> registers. Rows past skv are clamped to the last
-// key (finite values; their scores are masked).
-__device__ __forceinline__ void load_k(u32x4 (&st)[2], const FlashArgs &a, const half_t *kh, int key0,
-                                       const TileOffsets &t) {
-    if (key0 + BN <= a.skv) {
-        const half_t *kt = kh + (int64_t)key0 * D;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) st[p] = ldg16(kt + t.kg[p]);
-    } else {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int key = min(key0 + t.krow[p], a.skv - 1);
-            st[p] = ldg16(kh + (int64_t)key * D + (t.kg[p] - t.krow[p] * D));
+    for (int n = 0; n < 32; ++n) {
+        const half8 a = fr[n % RA];
+        const int m = n + RA;
+        fr[n % RA] = rd(m < 32 ? cur + m * FRAG : nxt + (m - 32) * FRAG);
+        if (n < 16) {
+            const int kk = n >> 1, kb = n & 1;
+            sn[kb] = mfma32(a, qf[kk], kk == 0 ? floatx16{} : sn[kb]);
+        } else {
+            const int mb = (n - 16) & 3, ks = (n - 16) >> 2;
+            o[mb] = mfma32(a, pf[ks], o[mb]);
         }
     }
+    l_run += row_sum(sc);
+    update_max(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
+    barrier_no_fence();
 }
 
-// V^T tile starting at key0 -> registers; keys past skv are zero so that the
-// masked probabilities multiply zeros.
-__device__ __forceinline__ void load_v(u32x4 (&st)[2], const FlashArgs &a, const half_t *vh, int key0,
-                                       const TileOffsets &t) {
-    const half_t *vt = vh + key0;
-    if (key0 + BN <= a.skv) {
+// Any step t (the last few of the loop): the same work with every condition
+// checked, and without reading ahead into the next step.
+__device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
+                                             floatx16 (&o)[4], const half8 (&qf)[8], float &m_run,
+                                             float &l_run) {
+    const int inflight = issue_stage(c, t + 3);
+    const half_t *cur = c.rl + (t & 3) * SLOT;
+    half8 pf[4];
+    exp_and_pack(sc, pf, -m_run * kLog2e);
+    const bool has_s = t + 1 < c.T;
+    if (has_s) {
+        half8 fa[16];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) st[p] = ldg16(vt + t.vg[p]);
-    } else {
+        for (int n = 0; n < 16; ++n) fa[n] = rd(cur + n * FRAG);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int kstart = key0 + t.vkey[p];
-            const half_t *src = vt + t.vg[p];
-            half8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (kstart + e < a.skv) ? src[e] : (half_t)0.0f;
-            st[p] = as_u32x4(v);
+        for (int n = 0; n < 16; ++n) {
+            const int kk = n >> 1, kb = n & 1;
+            sn[kb] = mfma32(fa[n], qf[kk], kk == 0 ? floatx16{} : sn[kb]);
         }
+    }
+    {
+        half8 fb[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) fb[n] = rd(cur + (NFRAG + n) * FRAG);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) o[n & 3] = mfma32(fb[n], pf[n >> 2], o[n & 3]);
+    }
+    l_run += row_sum(sc);
+    if (has_s) {
+        const int key0 = (t + 1) * BN;
+        const float mt = (key0 + BN <= c.skv) ? row_max<false>(sn, key0, c.skv, c.lane >> 5)
+                                               : row_max<true>(sn, key0, c.skv, c.lane >> 5);
+        update_max(mt, m_run, l_run, o);
+        wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
+        barrier_no_fence();
     }
 }
 
-__device__ __forceinline__ void store_k(const u32x4 (&st)[2], half_t *ks, const TileOffsets &t) {
+__device__ __forceinline__ void swap_s(floatx16 (&a)[2], floatx16 (&b)[2]) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4 *>(ks + t.kl[p]) = st[p];
+    for (int kb = 0; kb < 2; ++kb) {
+        const floatx16 t = a[kb];
+        a[kb] = b[kb];
+        b[kb] = t;
+    }
 }
 
-__device__ __forceinline__ void store_v(const u32x4 (&st)[2], half_t *vs, const TileOffsets &t) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4 *>(vs + t.vl[p]) = st[p];
-}
-
-__device__ __forceinline__ void softmax_tile(floatx16 (&s)[2], half8 (&pf)[2][2], floatx16 (&o)[4],
-                                             float &m_run, float &l_run, int lane, int j, int skv) {
-    if ((j + 1) * BN <= skv)
-        softmax_phase<false>(s, pf, o, m_run, l_run, lane, j * BN, skv);
-    else
-        softmax_phase<true>(s, pf, o, m_run, l_run, lane, j * BN, skv);
-}
-
-// Tile j holds K_j in ksm[j % 2] and V_j in vsm[j % 2]. Step j computes
-// S_j = K_j Q^T and O += V_{j-1} P_{j-1}, then the softmax of S_j; meanwhile
-// K_{j+1} and V_j are loaded into registers and stored at the end of the step
-// into ksm[(j+1) % 2] and vsm[j % 2]. Both buffers were last read in step j-1,
-// which every wave finished before the barrier that ended it; the barrier at
-// the end of step j publishes them. A final step adds V_{T-1} P_{T-1}.
+// Stage s holds K_{s+1} and V_s; the prologue loads K_0 as stage -1 (slot 3)
+// and stages 0..2, computes S_0 and its row max. Step t (0 <= t < T) adds
+// V_t P_t into O and computes S_{t+1}; it issues stage t+3 into the slot that
+// stage t-1 used (all of whose reads finished before the barrier that ended
+// step t-1) and ends by waiting for stage t+2 and a barrier, so step t+1 may
+// read stage t+1's operands ahead of that barrier.
 __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
-    __shared__ __attribute__((aligned(16))) half_t ksm[2 * K_TILE];
-    __shared__ __attribute__((aligned(16))) half_t vsm[2 * V_TILE];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -276,72 +341,85 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     const int qb = work % nqb;
 
     const half_t *qh = a.q + (int64_t)head * a.q_head_stride;
-    const half_t *kh = a.k + (int64_t)head * a.k_head_stride;
-    const half_t *vh = a.vt + (int64_t)head * a.v_head_stride;
-
     const int q = qb * BQ + wave * 32 + (lane & 31);
     const int qc = min(q, a.sq - 1);
     half8 qf[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 16 + 8 * h));
 
-    floatx16 o[4], s[2];
-    half8 pf[2][2];
+    floatx16 o[4], sa[2], sb[2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) o[mb] = floatx16{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int T = (a.skv + BN - 1) / BN;
+    Ctx c;
+    c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride);
+    c.vh = reinterpret_cast<const char *>(a.vt + (int64_t)head * a.v_head_stride);
+    c.ring = smem;
+    c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
+    c.lo = load_offsets(a, wave, lane);
+    c.wave = wave;
+    c.lane = lane;
+    c.skv = a.skv;
+    c.T = (a.skv + BN - 1) / BN;
+    c.vrs = a.v_row_stride;
+    const int T = c.T;
+
     if (T > 0) {
-        const TileOffsets toff = tile_offsets(a, tid);
-        u32x4 sk[2], sv[2];
-        load_k(sk, a, kh, 0, toff);
-        store_k(sk, ksm, toff);
-        __syncthreads();
-        // step 0: S_0 only
-        if (T > 1) load_k(sk, a, kh, BN, toff);
-        load_v(sv, a, vh, 0, toff);
-        mfma_phase<true, false>(ksm, vsm, qf, pf, s, o, lane);
-        softmax_tile(s, pf, o, m_run, l_run, lane, 0, a.skv);
-        if (T > 1) store_k(sk, ksm + K_TILE, toff);
-        store_v(sv, vsm, toff);
-        __syncthreads();
-        // Steady state: K_{j+1} and V_j are full tiles and S_j needs no mask,
-        // so the loads are branch-free and stay in flight across the MFMAs.
-        int j = 1;
-        for (; j + 2 < T; ++j) {
-            const half_t *kt = kh + (int64_t)(j + 1) * BN * D;
-            const half_t *vt = vh + j * BN;
+        issue_stage(c, -1);
+        issue_stage(c, 0);
+        issue_stage(c, 1);
+        wait_vm_lgkm(issue_stage(c, 2));  // stages -1, 0, 1 complete
+        barrier_no_fence();
+        {
+            const half_t *k0 = c.rl + 3 * SLOT;
+            half8 fa[16];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) sk[p] = ldg16(kt + toff.kg[p]);
+            for (int n = 0; n < 16; ++n) fa[n] = rd(k0 + n * FRAG);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) sv[p] = ldg16(vt + toff.vg[p]);
-            mfma_phase<true, true>(ksm + (j & 1) * K_TILE, vsm + ((j - 1) & 1) * V_TILE, qf, pf, s, o, lane);
-            softmax_phase<false>(s, pf, o, m_run, l_run, lane, j * BN, a.skv);
-            store_k(sk, ksm + ((j + 1) & 1) * K_TILE, toff);
-            store_v(sv, vsm + (j & 1) * V_TILE, toff);
-            __syncthreads();
+            for (int n = 0; n < 16; ++n) {
+                const int kk = n >> 1, kb = n & 1;
+                sa[kb] = mfma32(fa[n], qf[kk], kk == 0 ? floatx16{} : sa[kb]);
+            }
         }
-        // The last (at most two) steps, whose loads may touch the partial tile.
-        for (; j < T; ++j) {
-            if (j + 1 < T) load_k(sk, a, kh, (j + 1) * BN, toff);
-            load_v(sv, a, vh, j * BN, toff);
-            mfma_phase<true, true>(ksm + (j & 1) * K_TILE, vsm + ((j - 1) & 1) * V_TILE, qf, pf, s, o, lane);
-            softmax_tile(s, pf, o, m_run, l_run, lane, j, a.skv);
-            if (j + 1 < T) store_k(sk, ksm + ((j + 1) & 1) * K_TILE, toff);
-            store_v(sv, vsm + (j & 1) * V_TILE, toff);
-            __syncthreads();
+        const float mt = (BN <= a.skv) ? row_max<false>(sa, 0, a.skv, h) : row_max<true>(sa, 0, a.skv, h);
+        update_max(mt, m_run, l_run, o);
+        // Step 0 refills slot 3: every wave must be done reading K_0.
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+        barrier_no_fence();
+
+        // Steady steps need stage t+3 full (t + 4 <= last full tile) and run
+        // in pairs, so the two S register sets swap roles without copies.
+        const int last_full = (a.skv % BN == 0) ? T - 1 : T - 2;
+        const int n_steady = max(0, last_full - 3);
+        int t = 0;
+        if (n_steady >= 2) {
+            half8 fr[RA];
+#pragma unroll
+            for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
+            for (; t + 1 < n_steady; t += 2) {
+                steady_step(c, t, sa, sb, o, qf, fr, m_run, l_run);
+                steady_step(c, t + 1, sb, sa, o, qf, fr, m_run, l_run);
+            }
         }
-        mfma_phase<false, true>(ksm, vsm + ((T - 1) & 1) * V_TILE, qf, pf, s, o, lane);
+        for (; t < T; ++t) {
+            general_step(c, t, sa, sb, o, qf, m_run, l_run);
+            swap_s(sa, sb);
+        }
     }
 
-    if (q >= a.sq) return;
-    // ---- epilogue: combine the two lane halves' sums, normalise, store
+    // ---- epilogue: combine the two lane halves' sums, normalise, stage the
+    // wave's 32 x 128 block through LDS and store whole rows.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool empty = a.skv == 0;
     const float inv = empty ? 0.0f : 1.0f / l_tot;
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+    barrier_no_fence();  // every wave is done with the ring
+    const int q0 = qb * BQ + wave * 32;
+    const int rows = min(32, a.sq - q0);
+    const int qr = lane & 31;
     if (a.o32) {
-        float *dst = a.o32 + ((int64_t)head * a.sq + q) * D;
+        float *st = reinterpret_cast<float *>(smem) + wave * 32 * OP32;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -349,11 +427,23 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
                 floatx4 v;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) v[rr] = o[mb][4 * g + rr] * inv;
-                *reinterpret_cast<floatx4 *>(dst + 32 * mb + 8 * g + 4 * h) = v;
+                *reinterpret_cast<floatx4 *>(st + qr * OP32 + 32 * mb + 8 * g + 4 * h) = v;
             }
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+        __builtin_amdgcn_wave_barrier();
+        float *dst = a.o32 + ((int64_t)head * a.sq + q0) * D;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 2 * i + (lane >> 5), chunk = lane & 31;
+            if (row < rows)
+                *reinterpret_cast<floatx4 *>(dst + (int64_t)row * D + 4 * chunk) =
+                    *reinterpret_cast<const floatx4 *>(st + row * OP32 + 4 * chunk);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+        __builtin_amdgcn_wave_barrier();
     }
     if (a.o16) {
-        half_t *dst = a.o16 + (int64_t)q * a.o16_ld + (int64_t)head * D;
+        half_t *st = reinterpret_cast<half_t *>(smem) + wave * 32 * OP16;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -361,12 +451,21 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
                 half4 v;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) v[rr] = (half_t)(o[mb][4 * g + rr] * inv);
-                *reinterpret_cast<half4 *>(dst + 32 * mb + 8 * g + 4 * h) = v;
+                *reinterpret_cast<half4 *>(st + qr * OP16 + 32 * mb + 8 * g + 4 * h) = v;
             }
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+        __builtin_amdgcn_wave_barrier();
+        half_t *dst = a.o16 + (int64_t)q0 * a.o16_ld + (int64_t)head * D;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4), chunk = lane & 15;
+            if (row < rows)
+                *reinterpret_cast<u32x4 *>(dst + (int64_t)row * a.o16_ld + 8 * chunk) =
+                    *reinterpret_cast<const u32x4 *>(st + row * OP16 + 8 * chunk);
+        }
     }
-    if (a.lse && h == 0) {
-        a.lse[(int64_t)head * a.sq + q] =
-            empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
+    if (a.lse && h == 0 && q < a.sq) {
+        a.lse[(int64_t)head * a.sq + q] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
     }
 }
 

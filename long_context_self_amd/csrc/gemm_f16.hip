@@ -37,8 +37,6 @@ constexpr int SMEM_MAIN = STAGES * STAGE * 2;  // bytes
 constexpr int SMEM_EPI = BM * CP * 2;
 constexpr int SMEM_BYTES = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
 
 // LDS tile layout: 64-byte rows of four 16-byte chunks; logical chunk c of
 // row r sits at physical chunk c ^ swz(r), which spreads the 16 rows one LDS
@@ -47,17 +45,6 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 // reads, so a fragment address is one base register plus an immediate.
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
-// unconstrained (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
-// lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
-constexpr int vmcnt_only(int n) { return (n & 0xF) | 0x70 | 0xF00 | ((n >> 4) << 14); }
-
-// Workgroup barrier without the release fence of __syncthreads(): that fence
-// would wait for every in-flight global->LDS load (they count as LDS stores),
-// emptying the prefetch ring at each step. Visibility of a stage comes from
-// each wave's explicit vmcnt wait before the barrier; the memory clobber keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // Issue the direct global->LDS loads of one K-step (A rows and B rows) into
 // stage buffer `st`. A global_load_lds_dwordx4 writes 64 lanes x 16 bytes to
