@@ -103,22 +103,29 @@ struct Ctx {
 __device__ __forceinline__ char *slot_k(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2; }
 __device__ __forceinline__ char *slot_v(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2 + NFRAG * FRAG * 2; }
 
+// Buffer descriptor for raw byte addressing from `base` (stride 0, no
+// range clamp): the tile base lives in scalar registers and each lane adds
+// its loop-invariant 32-bit offset, so a direct load costs no vector ALU work.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, -1, 0x00020000);
+}
+
 // Full K tile `tile` -> K part of slot s (two direct loads per wave).
 __device__ __forceinline__ void issue_k_full(const Ctx &c, int tile, int s) {
-    const char *base = c.kh + (int64_t)tile * BN * D * 2;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.kh + (int64_t)tile * BN * D * 2);
     char *dst = slot_k(c, s) + 2 * c.wave * FRAG * 2;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-        __builtin_amdgcn_global_load_lds((gbl_void *)(base + c.lo.k[e]), (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + e * FRAG * 2), 16, c.lo.k[e], 0, 0, 0);
 }
 
 // Full V^T tile -> V part of slot s.
 __device__ __forceinline__ void issue_v_full(const Ctx &c, int tile, int s) {
-    const char *base = c.vh + (int64_t)tile * BN * 2;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.vh + (int64_t)tile * BN * 2);
     char *dst = slot_v(c, s) + 2 * c.wave * FRAG * 2;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-        __builtin_amdgcn_global_load_lds((gbl_void *)(base + c.lo.v[e]), (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + e * FRAG * 2), 16, c.lo.v[e], 0, 0, 0);
 }
 
 // Last, partial K tile: rows past skv are clamped to the last key (finite
@@ -191,25 +198,31 @@ __device__ __forceinline__ void wait_vm_lgkm(int n) {
 
 __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<const half8 *>(p); }
 
-// exp(S - m) in place (exp2 domain) and the fp16 B operands of the PV product.
-__device__ __forceinline__ void exp_and_pack(floatx16 (&sc)[2], half8 (&pf)[4], float mneg) {
+// P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
+// pf[ks] holds keys 32(ks / 2) + 16h + 8(ks % 2) + 0..7 of the lane's query.
+__device__ __forceinline__ void exp_and_pack(const floatx16 (&sc)[2], half8 (&pf)[4], float mneg) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kLog2e, mneg));
+        for (int i = 0; i < 16; ++i)
+            pf[2 * kb + (i >> 3)][i & 7] = (half_t)__builtin_amdgcn_exp2f(fmaf(sc[kb][i], kLog2e, mneg));
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Row sum of the fp16 probabilities (the very values the PV product
+// weights), two per dot instruction with fp32 accumulation.
+__device__ __forceinline__ float row_sum(const half8 (&pf)[4]) {
+    const half2v one = {(half_t)1.0f, (half_t)1.0f};
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[ks][j] = (half_t)sc[ks >> 1][8 * (ks & 1) + j];
-}
-
-__device__ __forceinline__ float row_sum(const floatx16 (&p)[2]) {
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a[i & 3] += p[kb][i];
-    return (a[0] + a[1]) + (a[2] + a[3]);
+        for (int j = 0; j < 4; j += 2) {
+            a0 = __builtin_amdgcn_fdot2(half2v{pf[ks][2 * j], pf[ks][2 * j + 1]}, one, a0, false);
+            a1 = __builtin_amdgcn_fdot2(half2v{pf[ks][2 * j + 2], pf[ks][2 * j + 3]}, one, a1, false);
+        }
+    return a0 + a1;
 }
 
 template <bool MASK>
@@ -221,12 +234,14 @@ __device__ __forceinline__ float row_max(floatx16 (&s)[2], int key0, int skv, in
             for (int i = 0; i < 16; ++i)
                 if (key0 + 32 * kb + 16 * h + i >= skv) s[kb][i] = -INFINITY;
     }
-    float a[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+    // two chains of three-operand maxima over the 32 scores
+    float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = (kb == 0 ? 4 : 0); i < 16; ++i) a[i & 3] = fmaxf(a[i & 3], s[kb][i]);
-    return wave_max_across_halves(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+    for (int i = 2; i < 16; i += 2) {
+        m0 = fmaxf(fmaxf(m0, s[0][i]), s[0][i + 1]);
+        m1 = fmaxf(fmaxf(m1, s[1][i]), s[1][i + 1]);
+    }
+    return wave_max_across_halves(fmaxf(m0, m1));
 }
 
 // New row max mt of the next scores: raise the reference max where it grew by
@@ -269,7 +284,7 @@ __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[
             o[mb] = mfma32(a, pf[ks], o[mb]);
         }
     }
-    l_run += row_sum(sc);
+    l_run += row_sum(pf);
     update_max(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
     barrier_no_fence();
@@ -302,7 +317,7 @@ __device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)
 #pragma unroll
         for (int n = 0; n < 16; ++n) o[n & 3] = mfma32(fb[n], pf[n >> 2], o[n & 3]);
     }
-    l_run += row_sum(sc);
+    l_run += row_sum(pf);
     if (has_s) {
         const int key0 = (t + 1) * BN;
         const float mt = (key0 + BN <= c.skv) ? row_max<false>(sn, key0, c.skv, c.lane >> 5)

@@ -13,8 +13,8 @@ import oracle
 from long_context_self_amd import binding as B
 from long_context_self_amd.synthetic import attention_inputs
 
-from .gpu_util import (REL_L2_F16, REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, partial, rel_l2, say,
-                       to_vt)
+from .gpu_util import (REL_L2_F16, REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, max_abs, partial, rel_l2,
+                       say, to_vt)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,7 +135,10 @@ def test_split_merge_equals_unsplit():
     r = rel_l2(o_m_heads, host(o_full))
     say(f"  merged vs unsplit rel_l2={r:.3e}")
     assert r <= REL_L2_SPLIT
-    assert rel_l2(host(lse_m), host(lse_full)) <= 1e-6
+    # Each partial's row sum adds the fp16-rounded probabilities (relative
+    # error below the fp16 unit roundoff 2^-11), so each LSE is within
+    # ln(1 + 2^-11) < 2^-11 of its exact value, and two of them within 2^-10.
+    assert max_abs(host(lse_m), host(lse_full)) <= 2.0 ** -10
     o_ref, lse_ref = oracle.partial_attention(q, k, v)
     assert_close(o_m_heads, o_ref, what="merged vs oracle")
     assert_close(host(lse_m), lse_ref, what="merged lse vs oracle")
