@@ -6,5 +6,5 @@ leg may import this package. The HIP library never does.
 
 from .mha import (  # noqa: F401
     as_f64, attention, block_forward, merge_heads, merge_partials,
-    partial_attention, project, scale_query, split_heads, stack_forward,
+    partial_attention, project, rms_norm, scale_query, split_heads, stack_forward,
 )

@@ -34,9 +34,11 @@ Sources, by page title and section:
 
 Readings where the pages are silent (each listed in the design notes):
 softmax scale 1/sqrt(d) applied to Q before QK^T; no biases; head j owns
-columns [j*d, (j+1)*d); RMSNorm, which the sample lists without placement or
-parameters, is left out; a KV block's partial output is normalised within the
+columns [j*d, (j+1)*d); a KV block's partial output is normalised within the
 block and carries its natural-log LSE; stacking is plain composition.
+RMSNorm, which the sample lists among the model's operations without placement
+or parameters, is optional here: when asked for, it normalises each token row
+of the block input (pre-norm) with eps 1e-6 and unit gain unless one is given.
 """
 
 from __future__ import annotations
@@ -45,9 +47,11 @@ import numpy as np
 
 __all__ = [
     "as_f64", "project", "scale_query", "split_heads", "merge_heads",
-    "attention", "partial_attention", "merge_partials", "block_forward",
+    "attention", "partial_attention", "merge_partials", "rms_norm", "block_forward",
     "stack_forward",
 ]
+
+RMS_EPS = 1e-6  # reading: the sample gives no epsilon
 
 ROW_BLOCK = 256  # query rows per softmax batch; memory only, no effect on values
 
@@ -151,16 +155,36 @@ def merge_partials(o_parts, lse_parts):
     return o, lse
 
 
-def block_forward(x, wq, wk, wv, wo, num_heads: int, rows=None, taps: bool = False):
+def rms_norm(x, gain=None, eps: float = RMS_EPS) -> np.ndarray:
+    """RMSNorm of every token row: x / sqrt(mean_j x_j^2 + eps), times gain.
+
+    The sample's self-attention model lists RMSNorm among its operations
+    ("Multi-Device Attention Inference with TensorRT", "Generating the ONNX
+    Models", Step 1), and the same page's introduction has each GPU normalise
+    its own tokens, i.e. the operation is local to a token. gain [h] defaults
+    to ones.
+    """
+    x = as_f64(x)
+    mean_sq = (x * x).mean(axis=-1, keepdims=True)
+    y = x / np.sqrt(mean_sq + eps)
+    if gain is not None:
+        y = y * as_f64(gain)
+    return y
+
+
+def block_forward(x, wq, wk, wv, wo, num_heads: int, rows=None, taps: bool = False, norm=None):
     """Forward pass of one block: y = Concat_j(attn_j) W_O.
 
     x [S, h]; rows selects the query rows to compute (all when None). K and V
     always come from all S rows; the result for a selected row is exact, not
-    an approximation. Returns y [len(rows), h], or with ``taps`` a dict with
-    q_scaled [H, R, d], k [H, S, d], v [H, S, d], o [R, h] (pre-projection),
-    lse [H, R] and y.
+    an approximation. norm = (gain or None, eps) applies RMSNorm to x first
+    (pre-norm); None leaves x as is. Returns y [len(rows), h], or with
+    ``taps`` a dict with q_scaled [H, R, d], k [H, S, d], v [H, S, d],
+    o [R, h] (pre-projection), lse [H, R] and y.
     """
     x = as_f64(x)
+    if norm is not None:
+        x = rms_norm(x, norm[0], norm[1])
     s, h = x.shape
     d = h // num_heads
     if rows is None:
@@ -177,9 +201,10 @@ def block_forward(x, wq, wk, wv, wo, num_heads: int, rows=None, taps: bool = Fal
     return y
 
 
-def stack_forward(x, layers, num_heads: int):
-    """Plain composition of blocks: x_{l+1} = Block_l(x_l) (multi-layer model)."""
+def stack_forward(x, layers, num_heads: int, norms=None):
+    """Plain composition of blocks: x_{l+1} = Block_l(x_l) (multi-layer model).
+    norms: None, or one (gain or None, eps) per layer for its pre-norm."""
     y = as_f64(x)
-    for (wq, wk, wv, wo) in layers:
-        y = block_forward(y, wq, wk, wv, wo, num_heads)
+    for i, (wq, wk, wv, wo) in enumerate(layers):
+        y = block_forward(y, wq, wk, wv, wo, num_heads, norm=None if norms is None else norms[i])
     return y

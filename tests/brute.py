@@ -63,3 +63,13 @@ def attention_one_head(q_scaled, k, v):
                     for col in zip(*v)])
         lses.append(m + math.log(z))
     return out, lses
+
+
+def rms_norm(x, gain, eps):
+    """Brute-force RMSNorm of each row: x_j / sqrt(mean of squares + eps) * g_j."""
+    out = []
+    for row in _tolist(x):
+        ms = math.fsum(v * v for v in row) / len(row)
+        inv = 1.0 / math.sqrt(ms + eps)
+        out.append([v * inv * (1.0 if gain is None else float(gain[j])) for j, v in enumerate(row)])
+    return out

@@ -19,6 +19,9 @@ pin. What each pin rests on:
 * merge          -- log-sum-exp merging of any key split equals the unsplit
                     result (online softmax, as Ring Attention streams K/V);
 * linearity      -- y is linear in W_O; W_V A pairs with A W_O.
+* RMSNorm        -- brute force; torch.nn.functional.rms_norm in float64 (and a
+                    torch pre-norm + MultiheadAttention block); closed forms of
+                    constant rows; invariants (unit mean square, scale and sign).
 """
 
 from __future__ import annotations
@@ -261,8 +264,88 @@ def pin_linearity(orc, tol=1e-12):
     return not bad, f"linearity errors {errs}"
 
 
+# -------------------------------------------------------------------- RMSNorm
+def pin_rmsnorm_bruteforce(orc, tol=1e-12):
+    worst = 0.0
+    for seed, (s, h, nh) in enumerate([(5, 4, 1), (7, 8, 2), (6, 6, 3)]):
+        rng = _rng(300 + seed)
+        x, (wq, wk, wv, wo) = _rand_block(rng, s, h)
+        x = x * rng.uniform(0.01, 3.0, size=(s, 1))  # rows of different magnitudes
+        g = rng.uniform(0.5, 1.5, size=h)
+        eps = [1e-6, 1e-3, 0.25][seed]
+        xn_b = brute.rms_norm(x, g, eps)
+        worst = max(worst, _rel(orc.rms_norm(x, g, eps), xn_b), _rel(orc.rms_norm(x, None, eps),
+                                                                     brute.rms_norm(x, None, eps)))
+        y_b, _, _ = brute.block(xn_b, wq, wk, wv, wo, nh)
+        worst = max(worst, _rel(orc.block_forward(x, wq, wk, wv, wo, nh, norm=(g, eps)), y_b))
+    return worst <= tol, f"max rel err vs brute-force RMSNorm {worst:.3e}"
+
+
+def pin_rmsnorm_torch(orc, tol=1e-10):
+    import torch
+    import torch.nn.functional as F
+
+    worst = 0.0
+    for seed, (s, h, nh) in enumerate([(64, 64, 4), (40, 96, 3)]):
+        rng = _rng(320 + seed)
+        x, (wq, wk, wv, wo) = _rand_block(rng, s, h)
+        g = rng.uniform(0.5, 1.5, size=h)
+        xt = torch.from_numpy(x)
+        ref_n = F.rms_norm(xt, (h,), weight=torch.from_numpy(g), eps=1e-6).numpy()
+        worst = max(worst, _rel(orc.rms_norm(x, g, 1e-6), ref_n))
+        mha = torch.nn.MultiheadAttention(h, nh, bias=False, batch_first=True, dtype=torch.float64)
+        with torch.no_grad():
+            mha.in_proj_weight.copy_(torch.from_numpy(np.concatenate([wq.T, wk.T, wv.T], 0)))
+            mha.out_proj.weight.copy_(torch.from_numpy(wo.T.copy()))
+            xn = torch.from_numpy(ref_n)[None]
+            ref, _ = mha(xn, xn, xn, need_weights=False)
+        worst = max(worst, _rel(orc.block_forward(x, wq, wk, wv, wo, nh, norm=(g, 1e-6)), ref[0].numpy()))
+    return worst <= tol, f"max rel err vs torch rms_norm (+ MultiheadAttention) {worst:.3e}"
+
+
+def pin_rmsnorm_closed_forms(orc, tol=1e-14):
+    # a constant row c*1 has mean square c^2: every entry becomes c / sqrt(c^2 + eps) * g_j
+    errs = []
+    g = np.array([1.0, 2.0, 0.5, -1.0])
+    for c, eps in [(3.0, 1e-6), (1e-3, 1e-6), (-2.0, 0.0), (0.5, 0.25)]:
+        x = np.full((1, 4), c)
+        want = c / math.sqrt(c * c + eps) * g
+        errs.append(float(np.max(np.abs(orc.rms_norm(x, g, eps)[0] - want))))
+    # alternating row (a, -a, a, -a): the same mean square a^2
+    a, eps = 2.0, 0.5
+    x = np.array([[a, -a, a, -a]])
+    want = np.array([a, -a, a, -a]) / math.sqrt(a * a + eps)
+    errs.append(float(np.max(np.abs(orc.rms_norm(x, None, eps)[0] - want))))
+    return max(errs) <= tol, f"RMSNorm closed-form errors {errs}"
+
+
+def pin_rmsnorm_invariants(orc, tol=1e-12):
+    rng = _rng(340)
+    x = rng.standard_normal((6, 10)) * rng.uniform(0.1, 5.0, size=(6, 1))
+    g = rng.uniform(0.5, 1.5, size=10)
+    errs = {}
+    y = orc.rms_norm(x, None, 0.0)
+    errs["unit_mean_square"] = float(np.max(np.abs((y * y).mean(axis=1) - 1.0)))
+    errs["scale"] = _rel(orc.rms_norm(3.7 * x, None, 0.0), y)
+    errs["sign"] = _rel(orc.rms_norm(-x, g, 1e-6), -orc.rms_norm(x, g, 1e-6))
+    errs["gain"] = _rel(orc.rms_norm(x, g, 1e-6), orc.rms_norm(x, None, 1e-6) * g)
+    # with eps = 0 a pre-normed block does not see the scale of its input rows
+    s, h, nh = 7, 8, 2
+    xb, (wq, wk, wv, wo) = _rand_block(rng, s, h)
+    lam = rng.uniform(0.2, 5.0, size=(s, 1))
+    gb = rng.uniform(0.5, 1.5, size=h)
+    errs["block_row_scale"] = _rel(orc.block_forward(lam * xb, wq, wk, wv, wo, nh, norm=(gb, 0.0)),
+                                   orc.block_forward(xb, wq, wk, wv, wo, nh, norm=(gb, 0.0)))
+    errs["block_norm_changes_output"] = 0.0 if _rel(
+        orc.block_forward(lam * xb, wq, wk, wv, wo, nh, norm=(gb, 0.0)),
+        orc.block_forward(lam * xb, wq, wk, wv, wo, nh)) > 1e-3 else 1.0
+    bad = {n: e for n, e in errs.items() if e > tol}
+    return not bad, f"RMSNorm invariant errors {errs}"
+
+
 ALL_PINS = [
     pin_bruteforce, pin_bruteforce_attention, pin_closed_forms, pin_torch_mha,
     pin_torch_sdpa, pin_invariants, pin_symmetries, pin_merge, pin_merge_rows,
-    pin_linearity,
+    pin_linearity, pin_rmsnorm_bruteforce, pin_rmsnorm_torch, pin_rmsnorm_closed_forms,
+    pin_rmsnorm_invariants,
 ]

@@ -43,6 +43,15 @@ MUTANTS = [
     ("merge_weight_sign", [("wn = np.exp(lse_parts - lse_safe[None])", "wn = np.exp(lse_safe[None] - lse_parts)")]),
     ("merge_lse_drops_max", [("m_safe + np.log(np.where(empty, 1.0, total))", "np.log(np.where(empty, 1.0, total))")]),
     ("merge_unnormalised", [("wn = np.exp(lse_parts - lse_safe[None])", "wn = np.exp(lse_parts - m_safe[None])")]),
+    ("rms_sum_not_mean", [("mean_sq = (x * x).mean(axis=-1, keepdims=True)",
+                           "mean_sq = (x * x).sum(axis=-1, keepdims=True)")]),
+    ("rms_no_square", [("mean_sq = (x * x).mean(axis=-1, keepdims=True)",
+                        "mean_sq = np.abs(x).mean(axis=-1, keepdims=True)")]),
+    ("rms_eps_outside_sqrt", [("y = x / np.sqrt(mean_sq + eps)", "y = x / (np.sqrt(mean_sq) + eps)")]),
+    ("rms_gain_dropped", [("y = y * as_f64(gain)", "y = y")]),
+    ("rms_norm_skipped", [("x = rms_norm(x, norm[0], norm[1])", "x = x")]),
+    ("rms_norm_after_projection", [("x = rms_norm(x, norm[0], norm[1])", "x = x * 1.0"),
+                                   ("y = project(o, wo)", "y = project(o, wo) if norm is None else rms_norm(project(o, wo), norm[0], norm[1])")]),
 ]
 
 
