@@ -94,12 +94,17 @@ def stats(xs):
             "mean": float(xs.mean())}
 
 
-def run_block(torch, B, hip, seq, h, nh, layers, warmup, steps, seed=0):
-    """Time `steps` forwards of a stack of `layers` blocks; per-kernel times from the events tap."""
+def run_block(torch, B, hip, seq, h, nh, layers, warmup, steps, seed=0, prenorm=False):
+    """Time `steps` forwards of a stack of `layers` blocks; per-kernel times from the events tap.
+    With `prenorm`, every block applies RMSNorm (unit gain, eps 1e-6) to its input; the row-norm
+    kernel then falls inside the "qkv" interval."""
     from long_context_self_amd.synthetic import block_inputs
 
     x, ws = block_inputs(seq, h, layers, dtype=np.float16, seed=seed)
     blocks = [B.AttnBlock(*(torch.from_numpy(w).cuda() for w in lw), num_heads=nh, max_tokens=seq) for lw in ws]
+    if prenorm:
+        for blk in blocks:
+            blk.set_prenorm(None, 1e-6)
     del ws
     xd = torch.from_numpy(x).cuda()
     del x
@@ -354,6 +359,16 @@ def main() -> int:
                           "oproj_tflops": f2["oproj"] / (k2["oproj"]["mean"] * 1e-3) / 1e12,
                           "block_tflops": sum(f2.values()) / (m2 * 1e-3) / 1e12})
             log(f"  {m2:.3f} ms/forward, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s")
+        log("block seq 8192 hidden 4096 with RMSNorm pre-norm")
+        mn, kn = run_block(torch, B, hip, seq, h, nh, 1, w, st, prenorm=True)
+        norm_bytes = seq * h * 2 + seq * 4
+        extra.append({"workload": "block forward with RMSNorm pre-norm (unit gain, eps 1e-6), seq 8192 hidden 4096 "
+                                  "heads 32 fp16", "ms_per_forward": mn,
+                      "qkv_with_norm_ms": kn["qkv"]["mean"], "qkv_without_norm_ms": kern["qkv"]["mean"],
+                      "norm_overhead_ms": kn["qkv"]["mean"] - kern["qkv"]["mean"],
+                      "norm_algorithmic_bytes": norm_bytes,
+                      "block_tflops": total_flops / (mn * 1e-3) / 1e12})
+        log(f"  {mn:.3f} ms/forward, norm overhead {extra[-1]['norm_overhead_ms'] * 1e3:.1f} us")
         log("rank share")
         extra.append(run_rank_share(torch, B, hip, w, st))
         log(f"  {extra[-1]['ms']:.3f} ms, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s, merge "

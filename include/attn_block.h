@@ -119,15 +119,40 @@ attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, a
                                 int64_t max_tokens, hipStream_t stream);
 
 /*
+ * attn_block_set_prenorm -- from now on, every attn_block_forward of `blk`
+ * first normalises each token row of x by RMSNorm (pre-norm):
+ *   x_i <- x_i / sqrt(mean_j x_ij^2 + eps) * gain.
+ * The sample's self-attention model lists RMSNorm among its operations
+ * ["Multi-Device Attention Inference with TensorRT", "Generating the ONNX
+ * Models", Step 1], and each GPU normalises its own tokens [same page,
+ * introduction]; the pages give neither its placement nor eps nor gain, so
+ * pre-norm on the block input is this library's reading and eps and gain
+ * are arguments (1e-6 and unit gain are the defaults of the reading).
+ *   gain  NULL (unit gain) or device [h] in the block's dtype, 4-byte
+ *         aligned. Folded once into the packed Q/K/V weights (rounded to the
+ *         block's dtype); the call synchronises `stream` before returning and
+ *         the caller may then free gain.
+ *   eps   finite and >= 0 (rows of zeros with eps = 0 give NaN, which
+ *         propagates).
+ * The per-row factor 1/sqrt(mean x^2 + eps) is computed by a row-reduction
+ * kernel and applied in the projection's epilogue; the normalised x is not
+ * written to memory. Allocates max_tokens floats of workspace on first use.
+ * Errors: ATTN_E_INVALID_ARG (NULL blk, eps not finite or < 0, pre-norm
+ * already enabled on blk), ATTN_E_OOM, ATTN_E_HIP.
+ */
+attn_status_t attn_block_set_prenorm(attn_block_t *blk, const void *gain, float eps, hipStream_t stream);
+
+/*
  * attn_block_forward -- y = Block(x) for an activation [seq][batch][hidden].
  *   x, y   device [seq][batch][h] in the block's dtype, 16-byte aligned; x and
  *          y must not overlap. y is not written when taps->qkv_only is set.
  *   seq    0 <= seq*batch <= max_tokens; seq = 0 enqueues nothing.
  *   batch  must be 1 (ATTN_E_UNSUPPORTED otherwise).
  *   taps   NULL, or caller buffers for intermediates (attn_taps_t).
- * Steps on `stream`: QKV projection with the head split and the 1/sqrt(d)
- * pre-scale fused into its epilogue; attention of every query row over all
- * seq keys; output projection. Not safe to run concurrently with another
+ * Steps on `stream`: (RMSNorm row factors, when pre-norm is enabled); QKV
+ * projection with the head split, the 1/sqrt(d) pre-scale (and the RMSNorm
+ * row factors) fused into its epilogue; attention of every query row over
+ * all seq keys; output projection. Not safe to run concurrently with another
  * forward of the same block (the workspace is shared).
  */
 attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int64_t seq,

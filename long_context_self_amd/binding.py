@@ -4,8 +4,8 @@ Argument marshalling only: every step runs in the library's HIP kernels.
 torch supplies device memory and the stream (``torch.cuda.current_stream()``
 unless one is passed). The functions keep the C names:
 
-* ``attn_block_create`` / ``attn_block_forward`` / ``attn_block_destroy``
-  (wrapped by the ``AttnBlock`` class),
+* ``attn_block_create`` / ``attn_block_set_prenorm`` / ``attn_block_forward`` /
+  ``attn_block_destroy`` (wrapped by the ``AttnBlock`` class),
 * ``attn_partial_forward``, ``attn_merge_lse``.
 
 There is no fallback: if the library is missing or fails to load, ``lib()``
@@ -26,8 +26,8 @@ ATTN_F16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_E_INVALID_ARG", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_OOM",
                 4: "ATTN_E_HIP"}
 
-EXPORTS = ("attn_block_create", "attn_block_forward", "attn_partial_forward", "attn_merge_lse",
-           "attn_block_destroy", "attn_last_error")
+EXPORTS = ("attn_block_create", "attn_block_set_prenorm", "attn_block_forward", "attn_partial_forward",
+           "attn_merge_lse", "attn_block_destroy", "attn_last_error")
 
 
 def vt_ld(seq: int) -> int:
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.attn_block_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, vp, vp, vp, vp, i64, vp]
     L.attn_block_create.restype = i32
+    L.attn_block_set_prenorm.argtypes = [vp, vp, ctypes.c_float, vp]
+    L.attn_block_set_prenorm.restype = i32
     L.attn_block_forward.argtypes = [vp, vp, vp, i64, i64, ctypes.POINTER(Taps), vp]
     L.attn_block_forward.restype = i32
     L.attn_partial_forward.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]
@@ -111,6 +113,10 @@ def attn_block_create(hidden: int, num_heads: int, wq, wk, wv, wo, max_tokens: i
     return handle.value
 
 
+def attn_block_set_prenorm(handle: int, gain=None, eps: float = 1e-6, stream=None) -> None:
+    _check(lib().attn_block_set_prenorm(handle, _ptr(gain), eps, _stream(stream)))
+
+
 def attn_block_forward(handle: int, x, y, seq: int, batch: int = 1, taps: Taps | None = None,
                        stream=None) -> None:
     _check(lib().attn_block_forward(handle, _ptr(x), _ptr(y), seq, batch,
@@ -149,6 +155,13 @@ class AttnBlock:
         self.dtype = wq.dtype
         self.max_tokens = max_tokens
         self.handle = attn_block_create(self.hidden, num_heads, wq, wk, wv, wo, max_tokens, stream)
+
+    def set_prenorm(self, gain=None, eps: float = 1e-6, stream=None) -> None:
+        """Enable RMSNorm of the input rows (pre-norm) for later forwards."""
+        if gain is not None and not (gain.is_cuda and gain.is_contiguous() and gain.dtype == self.dtype
+                                     and gain.numel() == self.hidden):
+            raise ValueError("gain must be a contiguous device tensor [h] of the block's dtype")
+        attn_block_set_prenorm(self.handle, gain, eps, stream)
 
     def forward(self, x, y=None, taps: Taps | None = None, stream=None):
         """x: [seq, 1, h] or [seq, h] device tensor; returns y of the same shape."""

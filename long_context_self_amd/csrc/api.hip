@@ -20,6 +20,9 @@ struct attn_block {
     void *w_qkv;  // fp16: [3h][h] = [W_Q|W_K|W_V]^T; fp32: [h][3h] = [W_Q|W_K|W_V]
     void *w_o;    // fp16: [h][h] = W_O^T;           fp32: [h][h] = W_O
     void *ws_q, *ws_k, *ws_vt, *ws_o;
+    int prenorm;      // RMSNorm of the input enabled (gain folded into w_qkv)
+    float norm_eps;
+    float *ws_rs;     // [max_tokens] per-row 1 / rms(x), when prenorm
 };
 
 namespace {
@@ -50,7 +53,7 @@ attn_status_t hip_fail(const char *where, hipError_t e) {
 
 void free_block(attn_block *b) {
     if (!b) return;
-    void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o};
+    void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o, b->ws_rs};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete b;
@@ -135,6 +138,28 @@ ATTN_API void attn_block_destroy(attn_block_t *blk) {
     (void)hipSetDevice(cur);
 }
 
+ATTN_API attn_status_t attn_block_set_prenorm(attn_block_t *blk, const void *gain, float eps, hipStream_t stream) {
+    Check c = validate_set_prenorm(blk == nullptr, eps, blk && blk->prenorm);
+    if (c.status != kOk) return report(c);
+    if (gain && !aligned(gain, 4)) return set_error(kInvalid, "attn_block_set_prenorm: gain misaligned");
+    if (!blk->ws_rs) {
+        hipError_t e = hipMalloc(reinterpret_cast<void **>(&blk->ws_rs), (size_t)blk->max_tokens * sizeof(float));
+        if (e != hipSuccess) {
+            blk->ws_rs = nullptr;
+            (void)hipGetLastError();
+            return set_error(kOom, "attn_block_set_prenorm: device allocation failed");
+        }
+    }
+    if (gain) {
+        HIP_TRY("attn_block_set_prenorm: gain folding",
+                launch_fold_gain(blk->w_qkv, blk->dt == kF16, blk->hidden, gain, stream));
+        HIP_TRY("attn_block_set_prenorm: hipStreamSynchronize", hipStreamSynchronize(stream));
+    }
+    blk->prenorm = 1;
+    blk->norm_eps = eps;
+    return ATTN_OK;
+}
+
 ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int64_t seq, int64_t batch,
                                           const attn_taps_t *taps, hipStream_t stream) {
     TapsView tv{};
@@ -158,6 +183,12 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
 #define MARK(i) \
     if (ev) HIP_TRY("attn_block_forward: hipEventRecord", hipEventRecord(ev[i], stream))
     MARK(0);
+    const float *row_scale = nullptr;
+    if (blk->prenorm) {
+        HIP_TRY("attn_block_forward: RMSNorm row scales",
+                launch_rms_rowscale(x, blk->dt == kF16, S, h, blk->norm_eps, blk->ws_rs, stream));
+        row_scale = blk->ws_rs;
+    }
 
     if (blk->dt == kF16) {
         GemmArgs g{};
@@ -176,6 +207,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.hidden = h;
         g.head_dim = d;
         g.q_scale = q_scale;
+        g.row_scale = row_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f16(g, stream));
         MARK(1);
         if (qkv_only) return ATTN_OK;
@@ -225,6 +257,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.hidden = h;
         g.head_dim = d;
         g.q_scale = q_scale;
+        g.row_scale = row_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f32(g, stream));
         MARK(1);
         if (qkv_only) return ATTN_OK;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void gemm_f32_nn(GemmArgsF32 g) {
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
             if (m >= g.M || n >= g.N) continue;
-            const float v = acc[i][j];
+            const float v = g.row_scale ? acc[i][j] * g.row_scale[m] : acc[i][j];
             if (g.mode == kPlain) {
                 g.c[(int64_t)m * g.ldc + n] = v;
             } else {

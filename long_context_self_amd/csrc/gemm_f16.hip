@@ -190,14 +190,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const int row = wm * 128 + i * 32 + 8 * gg + 4 * h;
+                // RMSNorm pre-norm: output row m scales by 1 / rms(x_m) (rows past M clamp)
+                float rsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (g.row_scale) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rsc[r] = g.row_scale[min(m0 + row + r, g.M - 1)];
+                }
                 if (v_tile) {
                     half4 v;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = (half_t)acc[i][j][4 * gg + r];
+                    for (int r = 0; r < 4; ++r) v[r] = (half_t)(acc[i][j][4 * gg + r] * rsc[r]);
                     *reinterpret_cast<half4 *>(smem + col * CP + row) = v;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) smem[(row + r) * CP + col] = (half_t)(acc[i][j][4 * gg + r] * sc);
+                    for (int r = 0; r < 4; ++r)
+                        smem[(row + r) * CP + col] = (half_t)(acc[i][j][4 * gg + r] * rsc[r] * sc);
                 }
             }
         }

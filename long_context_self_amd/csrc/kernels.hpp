@@ -60,6 +60,7 @@ struct GemmArgs {
     int64_t vt_ld;
     int hidden, head_dim;
     float q_scale;
+    const float *row_scale;  // nullable: output row m is multiplied by row_scale[m] (RMSNorm pre-norm)
 };
 
 // fp32 path: C[M][N] = A[M][K] * W[K][N] with W row-major (as given).
@@ -78,6 +79,7 @@ struct GemmArgsF32 {
     int64_t vt_ld;
     int hidden, head_dim;
     float q_scale;
+    const float *row_scale;  // nullable, as in GemmArgs
 };
 
 struct MergeArgs {
@@ -95,6 +97,11 @@ hipError_t launch_flash_fwd_f32(const FlashArgsF32 &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgsF32 &a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
+// RMSNorm pre-norm: rs[r] = 1 / sqrt(mean_j x[r][j]^2 + eps) for rows x [rows][h]
+// (fp16 when f16, else fp32); and w_qkv's input-feature rows scaled by gain.
+hipError_t launch_rms_rowscale(const void *x, bool f16, int64_t rows, int h, float eps, float *rs,
+                               hipStream_t stream);
+hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, const void *gain, hipStream_t stream);
 // dst[n][k] = src[k][n] for an [rows][cols] fp16 matrix (dst is [cols][rows]).
 hipError_t launch_transpose_f16(const _Float16 *src, int rows, int cols, _Float16 *dst,
                                 int64_t ld_dst, hipStream_t stream);

@@ -132,9 +132,18 @@ inline Check validate_partial(int num_heads, int head_dim, int dt, const void *q
         return fail(kInvalid, "attn_partial_forward: q_head_stride %lld < sq*head_dim", (long long)qhs);
     if (skv > 0) {
         if (vrs < skv) return fail(kInvalid, "attn_partial_forward: v_row_stride %lld < skv", (long long)vrs);
+        if (vrs > kMaxTokens)  // keeps every in-head V^T offset within 32 bits
+            return fail(kUnsupported, "attn_partial_forward: v_row_stride above %lld", (long long)kMaxTokens);
         if (num_heads > 1 && (khs < skv * head_dim || vhs < head_dim * vrs))
             return fail(kInvalid, "attn_partial_forward: k/v head strides smaller than one head");
     }
+    return ok();
+}
+
+inline Check validate_set_prenorm(bool blk_null, float eps, bool already_set) {
+    if (blk_null) return fail(kInvalid, "attn_block_set_prenorm: blk is NULL");
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(kInvalid, "attn_block_set_prenorm: eps must be finite and >= 0");
+    if (already_set) return fail(kInvalid, "attn_block_set_prenorm: pre-norm is already enabled on this block");
     return ok();
 }
 

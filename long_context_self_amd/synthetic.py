@@ -56,6 +56,13 @@ def block_inputs(seq: int, hidden: int, layers: int = 1, dtype=np.float16, seed:
     return _cast(x, dtype), weights
 
 
+def norm_gain(hidden: int, dtype=np.float16, seed: int = 0):
+    """RMSNorm gain [hidden] ~ U(0.5, 1.5) from its own seeded stream (the
+    default reading is unit gain; tests also use a non-trivial one)."""
+    rng = np.random.default_rng(seed + 7919)
+    return _cast(rng.uniform(0.5, 1.5, size=hidden).astype(np.float32), dtype)
+
+
 def attention_inputs(num_heads: int, sq: int, skv: int, head_dim: int, dtype=np.float16,
                      seed: int = 0, score_std: float = 1.0):
     """Return head-major ``(q_scaled [H,sq,d], k [H,skv,d], v [H,skv,d])``.

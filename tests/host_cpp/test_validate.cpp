@@ -3,6 +3,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <cmath>
+
 #include "validate.hpp"
 
 using namespace attnblk;
@@ -53,6 +55,15 @@ int main() {
     EXPECT(validate_partial(4, 64, kF16, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status ==
            kUnsupported);
     // merge
+    EXPECT(validate_set_prenorm(false, 1e-6f, false).status == kOk);
+    EXPECT(validate_set_prenorm(false, 0.0f, false).status == kOk);
+    EXPECT(validate_set_prenorm(true, 1e-6f, false).status == kInvalid);
+    EXPECT(validate_set_prenorm(false, -1e-6f, false).status == kInvalid);
+    EXPECT(validate_set_prenorm(false, NAN, false).status == kInvalid);
+    EXPECT(validate_set_prenorm(false, INFINITY, false).status == kInvalid);
+    EXPECT(validate_set_prenorm(false, 1e-6f, true).status == kInvalid);
+    EXPECT(validate_partial(32, 128, kF16, P, 4096, 4096 * 128, P, 4096, 32768 * 128, P, 128 * (kMaxTokens + 8),
+                            kMaxTokens + 8, F, F).status == kUnsupported);
     EXPECT(validate_merge(8, 32, 128, 4096, F, F, P, kF16, nullptr).status == kOk);
     EXPECT(validate_merge(0, 32, 128, 4096, F, F, P, kF16, nullptr).status == kInvalid);
     EXPECT(validate_merge(8, 32, 128, 4096, F, F, reinterpret_cast<const char *>(P) + 4, kF16, nullptr).status ==

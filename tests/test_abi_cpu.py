@@ -78,6 +78,11 @@ def test_forward_rejects_null_block(L):
     assert st == B.ATTN_E_INVALID_ARG and "blk is NULL" in _err(L)
 
 
+def test_set_prenorm_rejects_null_block(L):
+    st = L.attn_block_set_prenorm(None, None, ctypes.c_float(1e-6), None)
+    assert st == B.ATTN_E_INVALID_ARG and "blk is NULL" in _err(L)
+
+
 def test_partial_rejects(L):
     args = dict(nh=32, d=128, dt=B.ATTN_F16, q=FAKE, sq=256, qhs=256 * 128, k=FAKE, skv=512,
                 khs=512 * 128, v=FAKE, vhs=128 * 512, vrs=512, o=FAKE, lse=FAKE)
@@ -98,6 +103,8 @@ def test_partial_rejects(L):
     assert call(q=FAKE + 8) == B.ATTN_E_INVALID_ARG and "aligned" in _err(L)
     assert call(qhs=100 * 128) == B.ATTN_E_INVALID_ARG
     assert call(nh=0) == B.ATTN_E_INVALID_ARG
+    big = (1 << 24) + 8
+    assert call(vrs=big, vhs=128 * big) == B.ATTN_E_UNSUPPORTED and "v_row_stride" in _err(L)
     assert call(sq=0) == B.ATTN_OK  # nothing to do, nothing enqueued
 
 
