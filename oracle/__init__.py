@@ -8,3 +8,4 @@ from .mha import (  # noqa: F401
     as_f64, attention, block_forward, merge_heads, merge_partials,
     partial_attention, project, rms_norm, scale_query, split_heads, stack_forward,
 )
+from . import shares  # noqa: F401,E402

@@ -73,3 +73,49 @@ def rms_norm(x, gain, eps):
         inv = 1.0 / math.sqrt(ms + eps)
         out.append([v * inv * (1.0 if gain is None else float(gain[j])) for j, v in enumerate(row)])
     return out
+
+
+def ulysses_recv_blocks(t, n_ranks, rank, keys_last=False):
+    """Brute-force first all-to-all on nested lists: t [H][S][d] (or [H][d][S]
+    with keys_last); returns block p for every p as nested lists."""
+    hh = len(t)
+    hl = hh // n_ranks
+    heads = range(rank * hl, (rank + 1) * hl)
+    out = []
+    for p in range(n_ranks):
+        blk = []
+        for j in heads:
+            if keys_last:
+                s = len(t[j][0])
+                c = s // n_ranks
+                blk.append([[t[j][dd][p * c + i] for i in range(c)] for dd in range(len(t[j]))])
+            else:
+                s = len(t[j])
+                c = s // n_ranks
+                blk.append([list(t[j][p * c + i]) for i in range(c)])
+        out.append(blk)
+    return out
+
+
+def tp_share(x, wq, wk, wv, wo, num_heads, n_ranks, rank):
+    """Brute-force TP partial output of one rank (nested lists)."""
+    x, wq, wk, wv, wo = (_tolist(a) for a in (x, wq, wk, wv, wo))
+    s, h = len(x), len(x[0])
+    d = h // num_heads
+    hl = num_heads // n_ranks
+    cols = list(range(rank * hl * d, (rank + 1) * hl * d))
+    sub = lambda w: [[w[i][c] for c in cols] for i in range(h)]
+    q, k, v = matmul(x, sub(wq)), matmul(x, sub(wk)), matmul(x, sub(wv))
+    scale = 1.0 / math.sqrt(d)
+    o = [[0.0] * len(cols) for _ in range(s)]
+    for j in range(hl):
+        cc = range(j * d, (j + 1) * d)
+        for i in range(s):
+            sc = [scale * math.fsum(q[i][c] * k[t][c] for c in cc) for t in range(s)]
+            m = max(sc)
+            e = [math.exp(a - m) for a in sc]
+            z = math.fsum(e)
+            for c in cc:
+                o[i][c] = math.fsum(e[t] * v[t][c] for t in range(s)) / z
+    wo_rows = [wo[c] for c in cols]
+    return matmul(o, wo_rows)
