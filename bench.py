@@ -212,6 +212,120 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
     }
 
 
+def run_ulysses_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks=8, seed=0):
+    """Rank 0's Ulysses share: receive-side layout of the first all-to-all (its 4 heads' blocks from all 8
+    ranks -> full-sequence head-major), attention of those heads over all 32768 rows, receive-side layout of
+    the second all-to-all (8 blocks of its rows -> concatenated heads). Q/K/V are the block's own projection
+    (taps); the all-to-all blocks are slices of them, as the ranks' projections would send them."""
+    from long_context_self_amd.synthetic import block_inputs
+
+    d = h // nh
+    hl, ch = nh // ranks, seq // ranks
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
+    blk = B.AttnBlock(*(torch.from_numpy(w).cuda() for w in ws), num_heads=nh, max_tokens=seq)
+    q = torch.empty((nh, seq, d), dtype=torch.float16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((nh, d, B.vt_ld(seq)), dtype=torch.float16, device="cuda")
+    blk.forward(torch.from_numpy(x).cuda(), taps=B.Taps(q.data_ptr(), k.data_ptr(), vt.data_ptr(), None, None, 1,
+                                                           None))
+    torch.cuda.synchronize()
+    blk.close()
+    # what rank 0 receives from rank p: rows of chunk p for heads 0..hl-1
+    rq = torch.stack([q[:hl, p * ch:(p + 1) * ch] for p in range(ranks)]).contiguous()
+    rk = torch.stack([k[:hl, p * ch:(p + 1) * ch] for p in range(ranks)]).contiguous()
+    rvt = torch.stack([vt[:hl, :, p * ch:(p + 1) * ch] for p in range(ranks)]).contiguous()
+    del q, k, vt
+    gq = torch.empty((hl, seq, d), dtype=torch.float16, device="cuda")
+    gk = torch.empty_like(gq)
+    gvt = torch.empty((hl, d, B.vt_ld(seq)), dtype=torch.float16, device="cuda")
+    o = torch.empty((seq, hl * d), dtype=torch.float16, device="cuda")
+    recv_o = torch.randn((ranks, ch, hl * d), device="cuda").half()
+    o_full = torch.empty((ch, h), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = hip.events(4 * steps)
+
+    def one(s):
+        if s is not None:
+            hip.record(evs[4 * s], stream)
+        B.attn_ulysses_gather(ranks, hl, d, seq, rq, rk, rvt, gq, gk, gvt)
+        if s is not None:
+            hip.record(evs[4 * s + 1], stream)
+        B.attn_heads_forward(hl, d, gq, gk, gvt, seq, o, hl * d)
+        if s is not None:
+            hip.record(evs[4 * s + 2], stream)
+        B.attn_ulysses_unpack_o(ranks, nh, d, ch, recv_o, o_full)
+        if s is not None:
+            hip.record(evs[4 * s + 3], stream)
+
+    for _ in range(warmup):
+        one(None)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        one(s)
+    torch.cuda.synchronize()
+    g = stats([hip.ms(evs[4 * s], evs[4 * s + 1]) for s in range(steps)])
+    a = stats([hip.ms(evs[4 * s + 1], evs[4 * s + 2]) for s in range(steps)])
+    u = stats([hip.ms(evs[4 * s + 2], evs[4 * s + 3]) for s in range(steps)])
+    hip.destroy(evs)
+    flops = 4.0 * seq * seq * hl * d
+    gather_bytes = 2 * 3 * hl * seq * d * 2
+    unpack_bytes = 2 * ch * h * 2
+    del rq, rk, rvt, gq, gk, gvt, o, recv_o, o_full
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"Ulysses share: rank 0 of {ranks}, {hl} of {nh} heads over seq {seq}, hidden {h}",
+        "ms": g["median"] + a["median"] + u["median"], "gather_ms": g, "attention_ms": a, "unpack_ms": u,
+        "attention_tflops": flops / (a["median"] * 1e-3) / 1e12,
+        "attention_frac_of_peak": flops / (a["median"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "gather_gbs": gather_bytes / (g["median"] * 1e-3) / 1e9, "gather_bytes": gather_bytes,
+        "unpack_gbs": unpack_bytes / (u["median"] * 1e-3) / 1e9, "unpack_bytes": unpack_bytes,
+    }
+
+
+def run_tp_share(torch, B, hip, warmup, steps, seq=8192, h=4096, nh=32, ranks=8, seed=0):
+    """Rank 0's tensor-parallel share: Q/K/V for its 4 heads (column shard), their attention, and the
+    partial output through its row shard of W_O."""
+    from long_context_self_amd.synthetic import block_inputs
+
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
+    blk = B.AttnBlock(*(torch.from_numpy(w).cuda() for w in ws), num_heads=nh, max_tokens=seq, n_ranks=ranks,
+                      rank=0)
+    del ws
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = hip.events(4 * steps)
+
+    def one(s):
+        taps = None
+        if s is not None:
+            taps = B.Taps(None, None, None, None, None, 0,
+                          ctypes.addressof(evs) + 4 * s * ctypes.sizeof(ctypes.c_void_p))
+        blk.forward(xd, y, taps=taps)
+
+    for _ in range(warmup):
+        one(None)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        one(s)
+    torch.cuda.synchronize()
+    st = {n: stats([hip.ms(evs[4 * s + i], evs[4 * s + i + 1]) for s in range(steps)])
+          for i, n in enumerate(("qkv", "attn", "oproj"))}
+    step = stats([hip.ms(evs[4 * s], evs[4 * s + 3]) for s in range(steps)])
+    hip.destroy(evs)
+    blk.close()
+    del xd, y
+    torch.cuda.empty_cache()
+    w = h // ranks
+    fl = {"qkv": 6.0 * seq * h * w, "attn": 4.0 * seq * seq * w, "oproj": 2.0 * seq * w * h}
+    return {
+        "workload": f"tensor-parallel share: rank 0 of {ranks} ({nh // ranks} heads), seq {seq}, hidden {h}, "
+                    "partial output before the all-reduce",
+        "ms_per_forward": step["median"], "kernels_ms": st,
+        "kernels_tflops": {n: fl[n] / (st[n]["median"] * 1e-3) / 1e12 for n in fl},
+        "share_tflops": sum(fl.values()) / (step["median"] * 1e-3) / 1e12,
+    }
+
 COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_counters_seq8192_h4096.txt")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_self_amd", "csrc")
 
@@ -373,6 +487,13 @@ def main() -> int:
         extra.append(run_rank_share(torch, B, hip, w, st))
         log(f"  {extra[-1]['ms']:.3f} ms, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s, merge "
             f"{extra[-1]['merge_gbs']:.0f} GB/s")
+        log("Ulysses share (rank 0 of 8), seq 32768")
+        extra.append(run_ulysses_share(torch, B, hip, w, st))
+        log(f"  {extra[-1]['ms']:.3f} ms: gather {extra[-1]['gather_gbs']:.0f} GB/s, attention "
+            f"{extra[-1]['attention_tflops']:.0f} TFLOP/s, unpack {extra[-1]['unpack_gbs']:.0f} GB/s")
+        log("tensor-parallel share (rank 0 of 8), seq 8192")
+        extra.append(run_tp_share(torch, B, hip, w, st))
+        log(f"  {extra[-1]['ms_per_forward']:.3f} ms/forward, {extra[-1]['share_tflops']:.0f} TFLOP/s")
         log("6 stacked blocks seq 32768")
         m6, k6 = run_block(torch, B, hip, 32768, 4096, 32, 6, 1, 3)
         f6 = block_flops(32768, 4096)

@@ -119,6 +119,31 @@ attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, a
                                 int64_t max_tokens, hipStream_t stream);
 
 /*
+ * attn_block_create_shard -- like attn_block_create, for one rank's share of
+ * tensor parallelism over n_ranks GPUs: W_Q, W_K, W_V are split by columns
+ * and W_O by rows, so the rank owns heads [rank*H/N, (rank+1)*H/N) and its
+ * forward returns the PARTIAL output y_r = O_r W_O[rows of its heads], the
+ * term the all-reduce sums (sum over ranks = the unsharded block's y).
+ * ["Tensor Parallelism: Sharding Weights for Parallel Layer Execution",
+ * section 1 (column- and row-wise splits of Y = X A) and section 3, steps
+ * 1-4 (heads split across GPUs, local attention, row-split W_O, all-reduce).]
+ *   hidden, num_heads, dt, max_tokens   as for attn_block_create (the full
+ *            block's sizes);
+ *   n_ranks  >= 1, divides num_heads;  rank  0 <= rank < n_ranks;
+ *   wq,wk,wv,wo  the FULL device [h][h] weights; only the rank's columns of
+ *            W_Q/W_K/W_V and rows of W_O are copied (the caller may free them
+ *            after the call, which synchronises `stream`).
+ * attn_block_forward then takes x [seq][h] (replicated) and writes the
+ * partial y [seq][h]; its taps hold the rank's heads only (H/N heads,
+ * attn_out [seq][(H/N)*d]). attn_block_set_prenorm applies as for a full block.
+ * Errors: those of attn_block_create, plus ATTN_E_INVALID_ARG for n_ranks,
+ * rank or num_heads % n_ranks.
+ */
+attn_status_t attn_block_create_shard(attn_block_t **out, int hidden, int num_heads, int n_ranks, int rank,
+                                      attn_dtype_t dt, const void *wq, const void *wk, const void *wv,
+                                      const void *wo, int64_t max_tokens, hipStream_t stream);
+
+/*
  * attn_block_set_prenorm -- from now on, every attn_block_forward of `blk`
  * first normalises each token row of x by RMSNorm (pre-norm):
  *   x_i <- x_i / sqrt(mean_j x_ij^2 + eps) * gain.
@@ -181,6 +206,59 @@ attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt,
                                    const void *k, int64_t skv, int64_t k_head_stride,
                                    const void *v_t, int64_t v_head_stride, int64_t v_row_stride,
                                    float *o_part, float *lse_part, hipStream_t stream);
+
+/*
+ * attn_heads_forward -- attention of num_heads heads over the full sequence,
+ * output token-major: o[i][j*d + c] for row i, head j. This is the block's
+ * attention step on its own; under Ulysses context parallelism a rank runs it
+ * on its subset of heads for every row of the sequence. [Scaled dot-product
+ * attention per head, "Tensor Parallelism: Sharding Weights for Parallel
+ * Layer Execution", section 3, step 3; Ulysses: news summary of "Scaling AI
+ * Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+ * Inference Support", the three context-parallel implementations.]
+ *   q_scaled, k  [H][seq][d] contiguous (q already times 1/sqrt(d));
+ *   v_t          [H][d][ATTN_VT_LD(seq)] (V transposed per head);
+ *   o            [seq][o_ld] in dt, o_ld >= H*d and a multiple of 8 (fp16)
+ *                or 4 (fp32);
+ *   lse          NULL or fp32 [H][seq], natural-log.
+ * head_dim 128 (ATTN_F16) or 64/128 (ATTN_F32); pointers 16-byte aligned.
+ * seq = 0 enqueues nothing.
+ */
+attn_status_t attn_heads_forward(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
+                                 const void *k, const void *v_t, int64_t seq, void *o, int64_t o_ld,
+                                 float *lse, hipStream_t stream);
+
+/*
+ * attn_ulysses_gather -- receive side of Ulysses' first all-to-all. Rank p
+ * holds rows [p*S/N, (p+1)*S/N) and projects them head-major; the slice of
+ * its heads that belongs to rank r is contiguous, and the all-to-all delivers
+ * it to r as block p. This call lays rank r's N blocks out as the full
+ * sequence of its H/N heads, ready for attn_heads_forward. [News summary of
+ * "Scaling AI Inference Across Multiple GPUs Using NVIDIA TensorRT with
+ * Multi-Device Inference Support", the three context-parallel
+ * implementations (DeepSpeed Ulysses: all-to-all on Q, K, V; every GPU gets
+ * the whole sequence for a subset of heads).]
+ *   n_ranks N >= 1; num_heads_local Hl = H/N; seq S with S/N a multiple of 8.
+ *   recv_q, recv_k  [N][Hl][S/N][d];   recv_vt  [N][Hl][d][S/N]
+ *   q_scaled, k     [Hl][S][d];        v_t      [Hl][d][ATTN_VT_LD(S)] (= S)
+ * Pure data movement (bit-exact). Buffers 16-byte aligned, not overlapping.
+ */
+attn_status_t attn_ulysses_gather(int n_ranks, int num_heads_local, int head_dim, attn_dtype_t dt, int64_t seq,
+                                  const void *recv_q, const void *recv_k, const void *recv_vt,
+                                  void *q_scaled, void *k, void *v_t, hipStream_t stream);
+
+/*
+ * attn_ulysses_unpack_o -- receive side of Ulysses' second all-to-all. Rank r
+ * writes its heads' output token-major [S][Hl*d]; rows [p*S/N, (p+1)*S/N) of
+ * it go back to rank p, which receives N such blocks, one per r. This call
+ * puts rank p's blocks in the concatenated-heads layout [S/N][H*d] that the
+ * output projection reads (block r fills columns [r*Hl*d, (r+1)*Hl*d)).
+ * [Same source: a second all-to-all restores the head and sequence layout.]
+ *   n_ranks N; num_heads H (a multiple of N); rows = S/N.
+ *   recv_o  [N][rows][(H/N)*d];  o  [rows][H*d].  Bit-exact data movement.
+ */
+attn_status_t attn_ulysses_unpack_o(int n_ranks, int num_heads, int head_dim, attn_dtype_t dt, int64_t rows,
+                                    const void *recv_o, void *o, hipStream_t stream);
 
 /*
  * attn_merge_lse -- combine n_parts partial results of the same query rows

@@ -6,7 +6,9 @@ unless one is passed). The functions keep the C names:
 
 * ``attn_block_create`` / ``attn_block_set_prenorm`` / ``attn_block_forward`` /
   ``attn_block_destroy`` (wrapped by the ``AttnBlock`` class),
-* ``attn_partial_forward``, ``attn_merge_lse``.
+* ``attn_block_create_shard`` (tensor-parallel share, ``AttnBlock(..., n_ranks=, rank=)``),
+* ``attn_partial_forward``, ``attn_merge_lse``, ``attn_heads_forward``,
+* ``attn_ulysses_gather``, ``attn_ulysses_unpack_o``.
 
 There is no fallback: if the library is missing or fails to load, ``lib()``
 raises, and every call raises ``AttnError`` on a non-OK status.
@@ -26,8 +28,9 @@ ATTN_F16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_E_INVALID_ARG", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_OOM",
                 4: "ATTN_E_HIP"}
 
-EXPORTS = ("attn_block_create", "attn_block_set_prenorm", "attn_block_forward", "attn_partial_forward",
-           "attn_merge_lse", "attn_block_destroy", "attn_last_error")
+EXPORTS = ("attn_block_create", "attn_block_create_shard", "attn_block_set_prenorm", "attn_block_forward",
+           "attn_partial_forward", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
+           "attn_ulysses_unpack_o", "attn_block_destroy", "attn_last_error")
 
 
 def vt_ld(seq: int) -> int:
@@ -61,6 +64,14 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.attn_block_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, vp, vp, vp, vp, i64, vp]
     L.attn_block_create.restype = i32
+    L.attn_block_create_shard.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    L.attn_block_create_shard.restype = i32
+    L.attn_heads_forward.argtypes = [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp]
+    L.attn_heads_forward.restype = i32
+    L.attn_ulysses_gather.argtypes = [i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_ulysses_gather.restype = i32
+    L.attn_ulysses_unpack_o.argtypes = [i32, i32, i32, i32, i64, vp, vp, vp]
+    L.attn_ulysses_unpack_o.restype = i32
     L.attn_block_set_prenorm.argtypes = [vp, vp, ctypes.c_float, vp]
     L.attn_block_set_prenorm.restype = i32
     L.attn_block_forward.argtypes = [vp, vp, vp, i64, i64, ctypes.POINTER(Taps), vp]
@@ -113,6 +124,34 @@ def attn_block_create(hidden: int, num_heads: int, wq, wk, wv, wo, max_tokens: i
     return handle.value
 
 
+def attn_block_create_shard(hidden: int, num_heads: int, n_ranks: int, rank: int, wq, wk, wv, wo,
+                            max_tokens: int, stream=None) -> int:
+    handle = ctypes.c_void_p()
+    _check(lib().attn_block_create_shard(ctypes.byref(handle), hidden, num_heads, n_ranks, rank,
+                                         _dtype_code(wq.dtype), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), max_tokens,
+                                         _stream(stream)))
+    return handle.value
+
+
+def attn_heads_forward(num_heads: int, head_dim: int, q_scaled, k, v_t, seq: int, o, o_ld: int, lse=None,
+                       dtype: torch.dtype = torch.float16, stream=None) -> None:
+    _check(lib().attn_heads_forward(num_heads, head_dim, _dtype_code(dtype), _ptr(q_scaled), _ptr(k), _ptr(v_t), seq,
+                                    _ptr(o), o_ld, _ptr(lse), _stream(stream)))
+
+
+def attn_ulysses_gather(n_ranks: int, num_heads_local: int, head_dim: int, seq: int, recv_q, recv_k, recv_vt,
+                        q_scaled, k, v_t, dtype: torch.dtype = torch.float16, stream=None) -> None:
+    _check(lib().attn_ulysses_gather(n_ranks, num_heads_local, head_dim, _dtype_code(dtype), seq, _ptr(recv_q),
+                                     _ptr(recv_k), _ptr(recv_vt), _ptr(q_scaled), _ptr(k), _ptr(v_t),
+                                     _stream(stream)))
+
+
+def attn_ulysses_unpack_o(n_ranks: int, num_heads: int, head_dim: int, rows: int, recv_o, o,
+                          dtype: torch.dtype = torch.float16, stream=None) -> None:
+    _check(lib().attn_ulysses_unpack_o(n_ranks, num_heads, head_dim, _dtype_code(dtype), rows, _ptr(recv_o), _ptr(o),
+                                       _stream(stream)))
+
+
 def attn_block_set_prenorm(handle: int, gain=None, eps: float = 1e-6, stream=None) -> None:
     _check(lib().attn_block_set_prenorm(handle, _ptr(gain), eps, _stream(stream)))
 
@@ -145,7 +184,10 @@ def attn_merge_lse(n_parts: int, num_heads: int, head_dim: int, sq: int, o_parts
 class AttnBlock:
     """One self-attention block: packed weights + workspace in the library."""
 
-    def __init__(self, wq, wk, wv, wo, num_heads: int, max_tokens: int, stream=None):
+    def __init__(self, wq, wk, wv, wo, num_heads: int, max_tokens: int, stream=None, n_ranks: int = 1,
+                 rank: int = 0):
+        """With n_ranks > 1 the block is rank `rank`'s tensor-parallel share
+        (attn_block_create_shard): its forward returns the partial output."""
         for w in (wq, wk, wv, wo):
             if not (w.is_cuda and w.is_contiguous() and w.dim() == 2 and w.shape[0] == w.shape[1]):
                 raise ValueError("weights must be contiguous square device tensors [h, h]")
@@ -154,7 +196,12 @@ class AttnBlock:
         self.head_dim = self.hidden // num_heads
         self.dtype = wq.dtype
         self.max_tokens = max_tokens
-        self.handle = attn_block_create(self.hidden, num_heads, wq, wk, wv, wo, max_tokens, stream)
+        self.n_ranks, self.rank = n_ranks, rank
+        if n_ranks == 1 and rank == 0:
+            self.handle = attn_block_create(self.hidden, num_heads, wq, wk, wv, wo, max_tokens, stream)
+        else:
+            self.handle = attn_block_create_shard(self.hidden, num_heads, n_ranks, rank, wq, wk, wv, wo, max_tokens,
+                                                  stream)
 
     def set_prenorm(self, gain=None, eps: float = 1e-6, stream=None) -> None:
         """Enable RMSNorm of the input rows (pre-norm) for later forwards."""

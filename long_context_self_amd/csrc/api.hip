@@ -15,10 +15,15 @@
 using namespace attnblk;
 
 struct attn_block {
-    int hidden, heads, head_dim, dt, device;
+    int hidden;     // model width: x and y are [S][hidden]
+    int heads;      // heads this block computes (all of them, or one rank's share)
+    int head_dim;
+    int width;      // heads * head_dim: width of the block's Q, K, V and attention output
+    int n_ranks, rank;  // tensor-parallel shard (1, 0 for the whole block)
+    int dt, device;
     int64_t max_tokens;
-    void *w_qkv;  // fp16: [3h][h] = [W_Q|W_K|W_V]^T; fp32: [h][3h] = [W_Q|W_K|W_V]
-    void *w_o;    // fp16: [h][h] = W_O^T;           fp32: [h][h] = W_O
+    void *w_qkv;  // fp16: [3*width][hidden] = [W_Q|W_K|W_V]^T (this shard's columns); fp32: [hidden][3*width]
+    void *w_o;    // fp16: [hidden][width] = W_O^T (this shard's rows);              fp32: [width][hidden]
     void *ws_q, *ws_k, *ws_vt, *ws_o;
     int prenorm;      // RMSNorm of the input enabled (gain folded into w_qkv)
     float norm_eps;
@@ -63,22 +68,25 @@ void free_block(attn_block *b) {
 
 ATTN_API const char *attn_last_error(void) { return g_last_error; }
 
-ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, attn_dtype_t dt,
-                                         const void *wq, const void *wk, const void *wv, const void *wo,
-                                         int64_t max_tokens, hipStream_t stream) {
-    Check c = validate_create(out == nullptr, hidden, num_heads, (int)dt, wq, wk, wv, wo, max_tokens);
-    if (c.status != kOk) {
-        if (out) *out = nullptr;
-        return report(c);
-    }
+namespace {
+
+// Pack the weight shard of `rank` (heads [rank*H/N, (rank+1)*H/N): columns
+// [c0, c0+width) of W_Q, W_K, W_V and rows [c0, c0+width) of W_O) and
+// allocate the workspace. n_ranks = 1 is the whole block.
+attn_status_t create_block(attn_block_t **out, int hidden, int num_heads, int n_ranks, int rank, int dt,
+                           const void *wq, const void *wk, const void *wv, const void *wo, int64_t max_tokens,
+                           hipStream_t stream) {
     *out = nullptr;
     attn_block *b = new (std::nothrow) attn_block();
     if (!b) return set_error(kOom, "attn_block_create: host allocation failed");
     std::memset(b, 0, sizeof(*b));
     b->hidden = hidden;
-    b->heads = num_heads;
     b->head_dim = hidden / num_heads;
-    b->dt = (int)dt;
+    b->heads = num_heads / n_ranks;
+    b->width = b->heads * b->head_dim;
+    b->n_ranks = n_ranks;
+    b->rank = rank;
+    b->dt = dt;
     b->max_tokens = max_tokens;
     hipError_t e = hipGetDevice(&b->device);
     if (e != hipSuccess) {
@@ -86,14 +94,14 @@ ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num
         return hip_fail("attn_block_create: hipGetDevice", e);
     }
     const size_t es = elem_size(b->dt);
-    const size_t h = hidden;
-    const size_t qk_bytes = (size_t)max_tokens * h * es;
-    const size_t vt_bytes = (size_t)ATTN_VT_LD(max_tokens) * h * es;
+    const size_t h = hidden, w = b->width, c0 = (size_t)rank * w;
+    const size_t qk_bytes = (size_t)max_tokens * w * es;
+    const size_t vt_bytes = (size_t)ATTN_VT_LD(max_tokens) * w * es;
     struct {
         void **p;
         size_t bytes;
-    } allocs[] = {{&b->w_qkv, 3 * h * h * es}, {&b->w_o, h * h * es}, {&b->ws_q, qk_bytes},
-                  {&b->ws_k, qk_bytes},        {&b->ws_vt, vt_bytes},  {&b->ws_o, qk_bytes}};
+    } allocs[] = {{&b->w_qkv, 3 * w * h * es}, {&b->w_o, w * h * es}, {&b->ws_q, qk_bytes},
+                  {&b->ws_k, qk_bytes},        {&b->ws_vt, vt_bytes}, {&b->ws_o, qk_bytes}};
     for (auto &a : allocs) {
         e = hipMalloc(a.p, a.bytes);
         if (e != hipSuccess) {
@@ -105,19 +113,20 @@ ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num
     }
     const void *w3[3] = {wq, wk, wv};
     if (b->dt == kF16) {
-        for (int r = 0; r < 3; ++r) {
-            e = launch_transpose_f16(static_cast<const _Float16 *>(w3[r]), hidden, hidden,
-                                     static_cast<_Float16 *>(b->w_qkv) + (size_t)r * h * h, hidden, stream);
-            if (e != hipSuccess) break;
-        }
+        for (int r = 0; r < 3 && e == hipSuccess; ++r)
+            e = launch_transpose_f16(static_cast<const _Float16 *>(w3[r]) + c0, hidden, (int)w, hidden,
+                                     static_cast<_Float16 *>(b->w_qkv) + (size_t)r * w * h, hidden, stream);
         if (e == hipSuccess)
-            e = launch_transpose_f16(static_cast<const _Float16 *>(wo), hidden, hidden,
-                                     static_cast<_Float16 *>(b->w_o), hidden, stream);
+            e = launch_transpose_f16(static_cast<const _Float16 *>(wo) + c0 * h, (int)w, hidden, hidden,
+                                     static_cast<_Float16 *>(b->w_o), (int64_t)w, stream);
     } else {
         for (int r = 0; r < 3 && e == hipSuccess; ++r)
-            e = hipMemcpy2DAsync(static_cast<char *>(b->w_qkv) + r * h * es, 3 * h * es, w3[r], h * es, h * es, h,
+            e = hipMemcpy2DAsync(static_cast<char *>(b->w_qkv) + r * w * es, 3 * w * es,
+                                 static_cast<const char *>(w3[r]) + c0 * es, h * es, w * es, h,
                                  hipMemcpyDeviceToDevice, stream);
-        if (e == hipSuccess) e = hipMemcpyAsync(b->w_o, wo, h * h * es, hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(b->w_o, static_cast<const char *>(wo) + c0 * h * es, w * h * es,
+                               hipMemcpyDeviceToDevice, stream);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
@@ -126,6 +135,32 @@ ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num
     }
     *out = b;
     return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_API attn_status_t attn_block_create(attn_block_t **out, int hidden, int num_heads, attn_dtype_t dt,
+                                         const void *wq, const void *wk, const void *wv, const void *wo,
+                                         int64_t max_tokens, hipStream_t stream) {
+    Check c = validate_create(out == nullptr, hidden, num_heads, (int)dt, wq, wk, wv, wo, max_tokens);
+    if (c.status != kOk) {
+        if (out) *out = nullptr;
+        return report(c);
+    }
+    return create_block(out, hidden, num_heads, 1, 0, (int)dt, wq, wk, wv, wo, max_tokens, stream);
+}
+
+ATTN_API attn_status_t attn_block_create_shard(attn_block_t **out, int hidden, int num_heads, int n_ranks,
+                                               int rank, attn_dtype_t dt, const void *wq, const void *wk,
+                                               const void *wv, const void *wo, int64_t max_tokens,
+                                               hipStream_t stream) {
+    Check c = validate_create(out == nullptr, hidden, num_heads, (int)dt, wq, wk, wv, wo, max_tokens);
+    if (c.status == kOk) c = validate_shard(num_heads, n_ranks, rank);
+    if (c.status != kOk) {
+        if (out) *out = nullptr;
+        return report(c);
+    }
+    return create_block(out, hidden, num_heads, n_ranks, rank, (int)dt, wq, wk, wv, wo, max_tokens, stream);
 }
 
 ATTN_API void attn_block_destroy(attn_block_t *blk) {
@@ -152,7 +187,7 @@ ATTN_API attn_status_t attn_block_set_prenorm(attn_block_t *blk, const void *gai
     }
     if (gain) {
         HIP_TRY("attn_block_set_prenorm: gain folding",
-                launch_fold_gain(blk->w_qkv, blk->dt == kF16, blk->hidden, gain, stream));
+                launch_fold_gain(blk->w_qkv, blk->dt == kF16, blk->hidden, 3 * (int64_t)blk->width, gain, stream));
         HIP_TRY("attn_block_set_prenorm: hipStreamSynchronize", hipStreamSynchronize(stream));
     }
     blk->prenorm = 1;
@@ -170,7 +205,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
     if (c.status != kOk) return report(c);
     if (seq == 0) return ATTN_OK;
     const int S = (int)(seq * batch);
-    const int h = blk->hidden, d = blk->head_dim, H = blk->heads;
+    const int h = blk->hidden, d = blk->head_dim, H = blk->heads, wd = blk->width;
     const int64_t vt_ld = ATTN_VT_LD(S);
     const float q_scale = (float)(1.0 / std::sqrt((double)d));
     void *q = (taps && taps->q_scaled) ? taps->q_scaled : blk->ws_q;
@@ -197,14 +232,14 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.b = static_cast<const _Float16 *>(blk->w_qkv);
         g.ldb = h;
         g.M = S;
-        g.N = 3 * h;
+        g.N = 3 * wd;
         g.K = h;
         g.mode = kQkv;
         g.q = static_cast<_Float16 *>(q);
         g.k = static_cast<_Float16 *>(k);
         g.vt = static_cast<_Float16 *>(vt);
         g.vt_ld = vt_ld;
-        g.hidden = h;
+        g.hidden = wd;
         g.head_dim = d;
         g.q_scale = q_scale;
         g.row_scale = row_scale;
@@ -223,18 +258,18 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         fa.skv = S;
         fa.num_heads = H;
         fa.o16 = static_cast<_Float16 *>(o);
-        fa.o16_ld = h;
+        fa.o16_ld = wd;
         fa.lse = lse;
         HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
         MARK(2);
         GemmArgs go{};
         go.a = static_cast<const _Float16 *>(o);
-        go.lda = h;
+        go.lda = wd;
         go.b = static_cast<const _Float16 *>(blk->w_o);
-        go.ldb = h;
+        go.ldb = wd;
         go.M = S;
         go.N = h;
-        go.K = h;
+        go.K = wd;
         go.mode = kPlain;
         go.c = static_cast<_Float16 *>(y);
         go.ldc = h;
@@ -245,16 +280,16 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.a = static_cast<const float *>(x);
         g.lda = h;
         g.w = static_cast<const float *>(blk->w_qkv);
-        g.ldw = 3 * h;
+        g.ldw = 3 * wd;
         g.M = S;
-        g.N = 3 * h;
+        g.N = 3 * wd;
         g.K = h;
         g.mode = kQkv;
         g.q = static_cast<float *>(q);
         g.k = static_cast<float *>(k);
         g.vt = static_cast<float *>(vt);
         g.vt_ld = vt_ld;
-        g.hidden = h;
+        g.hidden = wd;
         g.head_dim = d;
         g.q_scale = q_scale;
         g.row_scale = row_scale;
@@ -274,18 +309,18 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         fa.num_heads = H;
         fa.head_dim = d;
         fa.otok = static_cast<float *>(o);
-        fa.otok_ld = h;
+        fa.otok_ld = wd;
         fa.lse = lse;
         HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f32(fa, stream));
         MARK(2);
         GemmArgsF32 go{};
         go.a = static_cast<const float *>(o);
-        go.lda = h;
+        go.lda = wd;
         go.w = static_cast<const float *>(blk->w_o);
         go.ldw = h;
         go.M = S;
         go.N = h;
-        go.K = h;
+        go.K = wd;
         go.mode = kPlain;
         go.c = static_cast<float *>(y);
         go.ldc = h;
@@ -357,5 +392,110 @@ ATTN_API attn_status_t attn_merge_lse(int n_parts, int num_heads, int head_dim, 
     m.out_f16 = out_dt == ATTN_F16;
     m.lse_out = lse_out;
     HIP_TRY("attn_merge_lse", launch_lse_merge(m, stream));
+    return ATTN_OK;
+}
+
+ATTN_API attn_status_t attn_heads_forward(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
+                                          const void *k, const void *v_t, int64_t seq, void *o, int64_t o_ld,
+                                          float *lse, hipStream_t stream) {
+    Check c = validate_heads_forward(num_heads, head_dim, (int)dt, q_scaled, k, v_t, seq, o, o_ld, lse);
+    if (c.status != kOk) return report(c);
+    if (seq == 0) return ATTN_OK;
+    const int64_t vt_ld = ATTN_VT_LD(seq);
+    if (dt == ATTN_F16) {
+        FlashArgs fa{};
+        fa.q = static_cast<const _Float16 *>(q_scaled);
+        fa.k = static_cast<const _Float16 *>(k);
+        fa.vt = static_cast<const _Float16 *>(v_t);
+        fa.q_head_stride = seq * head_dim;
+        fa.k_head_stride = seq * head_dim;
+        fa.v_head_stride = (int64_t)head_dim * vt_ld;
+        fa.v_row_stride = vt_ld;
+        fa.sq = (int)seq;
+        fa.skv = (int)seq;
+        fa.num_heads = num_heads;
+        fa.o16 = static_cast<_Float16 *>(o);
+        fa.o16_ld = o_ld;
+        fa.lse = lse;
+        HIP_TRY("attn_heads_forward", launch_flash_fwd_f16(fa, stream));
+    } else {
+        FlashArgsF32 fa{};
+        fa.q = static_cast<const float *>(q_scaled);
+        fa.k = static_cast<const float *>(k);
+        fa.vt = static_cast<const float *>(v_t);
+        fa.q_head_stride = seq * head_dim;
+        fa.k_head_stride = seq * head_dim;
+        fa.v_head_stride = (int64_t)head_dim * vt_ld;
+        fa.v_row_stride = vt_ld;
+        fa.sq = (int)seq;
+        fa.skv = (int)seq;
+        fa.num_heads = num_heads;
+        fa.head_dim = head_dim;
+        fa.otok = static_cast<float *>(o);
+        fa.otok_ld = o_ld;
+        fa.lse = lse;
+        HIP_TRY("attn_heads_forward", launch_flash_fwd_f32(fa, stream));
+    }
+    return ATTN_OK;
+}
+
+ATTN_API attn_status_t attn_ulysses_gather(int n_ranks, int num_heads_local, int head_dim, attn_dtype_t dt,
+                                           int64_t seq, const void *recv_q, const void *recv_k,
+                                           const void *recv_vt, void *q_scaled, void *k, void *v_t,
+                                           hipStream_t stream) {
+    Check c = validate_ulysses_gather(n_ranks, num_heads_local, head_dim, (int)dt, seq, recv_q, recv_k, recv_vt,
+                                      q_scaled, k, v_t);
+    if (c.status != kOk) return report(c);
+    if (seq == 0) return ATTN_OK;
+    const int64_t es = elem_size((int)dt), ch = seq / n_ranks, d = head_dim, hl = num_heads_local;
+    // Q, K: block p of head jj ([ch][d], contiguous) -> rows [p*ch, (p+1)*ch) of head jj
+    const void *srcs[2] = {recv_q, recv_k};
+    void *dsts[2] = {q_scaled, k};
+    for (int t = 0; t < 2; ++t) {
+        SegCopyArgs a{};
+        a.src = static_cast<const char *>(srcs[t]);
+        a.dst = static_cast<char *>(dsts[t]);
+        a.n_outer = (uint32_t)n_ranks;
+        a.n_inner = (uint32_t)hl;
+        a.src_so = hl * ch * d * es;
+        a.src_si = ch * d * es;
+        a.dst_so = ch * d * es;
+        a.dst_si = seq * d * es;
+        a.chunks_per_seg = (uint32_t)(ch * d * es / 16);
+        HIP_TRY("attn_ulysses_gather: Q/K", launch_seg_copy(a, stream));
+    }
+    // V^T: row (jj, c) of block p ([ch] keys, contiguous) -> keys [p*ch, (p+1)*ch) of that row
+    SegCopyArgs a{};
+    a.src = static_cast<const char *>(recv_vt);
+    a.dst = static_cast<char *>(v_t);
+    a.n_outer = (uint32_t)n_ranks;
+    a.n_inner = (uint32_t)(hl * d);
+    a.src_so = hl * d * ch * es;
+    a.src_si = ch * es;
+    a.dst_so = ch * es;
+    a.dst_si = ATTN_VT_LD(seq) * es;
+    a.chunks_per_seg = (uint32_t)(ch * es / 16);
+    HIP_TRY("attn_ulysses_gather: V^T", launch_seg_copy(a, stream));
+    return ATTN_OK;
+}
+
+ATTN_API attn_status_t attn_ulysses_unpack_o(int n_ranks, int num_heads, int head_dim, attn_dtype_t dt, int64_t rows,
+                                             const void *recv_o, void *o, hipStream_t stream) {
+    Check c = validate_ulysses_unpack(n_ranks, num_heads, head_dim, (int)dt, rows, recv_o, o);
+    if (c.status != kOk) return report(c);
+    if (rows == 0) return ATTN_OK;
+    const int64_t es = elem_size((int)dt), wl = (int64_t)(num_heads / n_ranks) * head_dim;
+    // block r, row i ([wl] columns) -> row i, columns [r*wl, (r+1)*wl)
+    SegCopyArgs a{};
+    a.src = static_cast<const char *>(recv_o);
+    a.dst = static_cast<char *>(o);
+    a.n_outer = (uint32_t)n_ranks;
+    a.n_inner = (uint32_t)rows;
+    a.src_so = rows * wl * es;
+    a.src_si = wl * es;
+    a.dst_so = wl * es;
+    a.dst_si = n_ranks * wl * es;
+    a.chunks_per_seg = (uint32_t)(wl * es / 16);
+    HIP_TRY("attn_ulysses_unpack_o", launch_seg_copy(a, stream));
     return ATTN_OK;
 }

@@ -239,13 +239,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     }
 }
 
-__global__ __launch_bounds__(256) void transpose_f16(const half_t *src, int rows, int cols, half_t *dst,
-                                                     int64_t ld_dst) {
+// dst[c][r] = src[r][c] for a rows x cols submatrix with row stride ld_src.
+__global__ __launch_bounds__(256) void transpose_f16(const half_t *src, int rows, int cols, int64_t ld_src,
+                                                     half_t *dst, int64_t ld_dst) {
     __shared__ half_t t[64][65];
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
         int r = i / 64, c = i % 64;
-        if (r0 + r < rows && c0 + c < cols) t[r][c] = src[(int64_t)(r0 + r) * cols + c0 + c];
+        if (r0 + r < rows && c0 + c < cols) t[r][c] = src[(int64_t)(r0 + r) * ld_src + c0 + c];
     }
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -263,10 +264,10 @@ hipError_t launch_gemm_f16(const GemmArgs &g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_f16(const half_t *src, int rows, int cols, half_t *dst, int64_t ld_dst,
+hipError_t launch_transpose_f16(const half_t *src, int rows, int cols, int64_t ld_src, half_t *dst, int64_t ld_dst,
                                 hipStream_t stream) {
     dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-    hipLaunchKernelGGL(transpose_f16, grid, dim3(256), 0, stream, src, rows, cols, dst, ld_dst);
+    hipLaunchKernelGGL(transpose_f16, grid, dim3(256), 0, stream, src, rows, cols, ld_src, dst, ld_dst);
     return hipGetLastError();
 }
 

@@ -82,6 +82,18 @@ struct GemmArgsF32 {
     const float *row_scale;  // nullable, as in GemmArgs
 };
 
+// Batch of equal contiguous segments: segment (o, i), o < n_outer, i < n_inner,
+// of chunks_per_seg 16-byte chunks, from src + o*src_so + i*src_si to
+// dst + o*dst_so + i*dst_si (byte strides).
+struct SegCopyArgs {
+    const char *src;
+    char *dst;
+    uint32_t n_outer, n_inner;
+    int64_t src_so, src_si, dst_so, dst_si;
+    uint32_t chunks_per_seg;
+    uint32_t blocks_per_seg;  // set by the launcher
+};
+
 struct MergeArgs {
     int n_parts, num_heads, head_dim;
     int64_t sq;
@@ -101,9 +113,10 @@ hipError_t launch_lse_merge(const MergeArgs &a, hipStream_t stream);
 // (fp16 when f16, else fp32); and w_qkv's input-feature rows scaled by gain.
 hipError_t launch_rms_rowscale(const void *x, bool f16, int64_t rows, int h, float eps, float *rs,
                                hipStream_t stream);
-hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, const void *gain, hipStream_t stream);
+hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, int64_t n_out, const void *gain, hipStream_t stream);
+hipError_t launch_seg_copy(SegCopyArgs a, hipStream_t stream);
 // dst[n][k] = src[k][n] for an [rows][cols] fp16 matrix (dst is [cols][rows]).
-hipError_t launch_transpose_f16(const _Float16 *src, int rows, int cols, _Float16 *dst,
+hipError_t launch_transpose_f16(const _Float16 *src, int rows, int cols, int64_t ld_src, _Float16 *dst,
                                 int64_t ld_dst, hipStream_t stream);
 
 }  // namespace attnblk

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void rms_rowscale_f32(const float *x, int64_t 
     if (lane == 0) rs[row] = 1.0f / sqrtf(ms + eps);
 }
 
-// Packed fp16 Q/K/V weights [3h][h] (row n = output feature, column k =
+// Packed fp16 Q/K/V weights [n_out][h] (row n = output feature, column k =
 // input feature): w[n][k] *= g[k], rounded to fp16 once.
 __global__ __launch_bounds__(256) void fold_gain_f16(half_t *w, int64_t n_rows, int h, const half_t *g) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void fold_gain_f16(half_t *w, int64_t n_rows, 
     w[i] = (half_t)((float)w[i] * (float)g[k]);
 }
 
-// fp32 weights [h][3h] (row k = input feature): w[k][n] *= g[k].
+// fp32 weights [h][n_out] (row k = input feature): w[k][n] *= g[k].
 __global__ __launch_bounds__(256) void fold_gain_f32(float *w, int h, int64_t n_cols, const float *g) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)h * n_cols) return;
@@ -87,15 +87,15 @@ hipError_t launch_rms_rowscale(const void *x, bool f16, int64_t rows, int h, flo
     return hipGetLastError();
 }
 
-hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, const void *gain, hipStream_t stream) {
-    const int64_t n = 3 * (int64_t)h * h;
+hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, int64_t n_out, const void *gain, hipStream_t stream) {
+    const int64_t n = n_out * h;
     const dim3 grid((unsigned)((n + 255) / 256));
     if (f16)
-        hipLaunchKernelGGL(fold_gain_f16, grid, dim3(256), 0, stream, static_cast<half_t *>(w_qkv), 3 * (int64_t)h,
-                           h, static_cast<const half_t *>(gain));
+        hipLaunchKernelGGL(fold_gain_f16, grid, dim3(256), 0, stream, static_cast<half_t *>(w_qkv), n_out, h,
+                           static_cast<const half_t *>(gain));
     else
-        hipLaunchKernelGGL(fold_gain_f32, grid, dim3(256), 0, stream, static_cast<float *>(w_qkv), h,
-                           3 * (int64_t)h, static_cast<const float *>(gain));
+        hipLaunchKernelGGL(fold_gain_f32, grid, dim3(256), 0, stream, static_cast<float *>(w_qkv), h, n_out,
+                           static_cast<const float *>(gain));
     return hipGetLastError();
 }
 

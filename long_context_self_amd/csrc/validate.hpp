@@ -147,6 +147,79 @@ inline Check validate_set_prenorm(bool blk_null, float eps, bool already_set) {
     return ok();
 }
 
+inline Check validate_shard(int num_heads, int n_ranks, int rank) {
+    if (n_ranks < 1) return fail(kInvalid, "attn_block_create_shard: n_ranks %d < 1", n_ranks);
+    if (num_heads % n_ranks != 0)
+        return fail(kInvalid, "attn_block_create_shard: num_heads %d is not a multiple of n_ranks %d", num_heads,
+                    n_ranks);
+    if (rank < 0 || rank >= n_ranks) return fail(kInvalid, "attn_block_create_shard: rank %d outside [0, %d)", rank,
+                                                 n_ranks);
+    return ok();
+}
+
+inline Check validate_heads_forward(int num_heads, int head_dim, int dt, const void *q, const void *k,
+                                    const void *vt, int64_t seq, const void *o, int64_t o_ld, const float *lse) {
+    if (!dtype_known(dt)) return fail(kInvalid, "attn_heads_forward: unknown dtype %d", dt);
+    if (num_heads < 1) return fail(kInvalid, "attn_heads_forward: num_heads %d < 1", num_heads);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "attn_heads_forward: head_dim %d not supported for dtype %d", head_dim, dt);
+    if (seq < 0) return fail(kInvalid, "attn_heads_forward: negative seq");
+    if (seq > kMaxTokens) return fail(kUnsupported, "attn_heads_forward: seq above %lld", (long long)kMaxTokens);
+    if (seq == 0) return ok();
+    if (!q || !k || !vt || !o) return fail(kInvalid, "attn_heads_forward: q, k, v_t or o is NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16))
+        return fail(kInvalid, "attn_heads_forward: q, k, v_t and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(kInvalid, "attn_heads_forward: lse misaligned");
+    if (o_ld < (int64_t)num_heads * head_dim || o_ld % vec_elems(dt))
+        return fail(kInvalid, "attn_heads_forward: o_ld %lld must be >= num_heads*head_dim and a multiple of %lld",
+                    (long long)o_ld, (long long)vec_elems(dt));
+    return ok();
+}
+
+// Ulysses layouts: seq split into n_ranks chunks of seq/n_ranks rows, each a
+// multiple of 8 so that every moved segment is a whole number of 16-byte
+// chunks (fp16) and V^T rows need no padding.
+inline Check validate_ulysses(const char *what, int n_ranks, int num_heads, int head_dim, int dt, int64_t seq) {
+    if (!dtype_known(dt)) return fail(kInvalid, "%s: unknown dtype %d", what, dt);
+    if (n_ranks < 1 || num_heads < 1) return fail(kInvalid, "%s: n_ranks and num_heads must be >= 1", what);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "%s: head_dim %d not supported for dtype %d", what, head_dim, dt);
+    if (seq < 0 || seq % n_ranks != 0 || (seq / n_ranks) % 8 != 0)
+        return fail(kInvalid, "%s: seq %lld must be n_ranks x a multiple of 8", what, (long long)seq);
+    if (seq > kMaxTokens) return fail(kUnsupported, "%s: seq above %lld", what, (long long)kMaxTokens);
+    return ok();
+}
+
+inline Check validate_ulysses_gather(int n_ranks, int num_heads_local, int head_dim, int dt, int64_t seq,
+                                     const void *rq, const void *rk, const void *rvt, const void *q, const void *k,
+                                     const void *vt) {
+    Check c = validate_ulysses("attn_ulysses_gather", n_ranks, num_heads_local, head_dim, dt, seq);
+    if (c.status != kOk || seq == 0) return c;
+    const void *ps[6] = {rq, rk, rvt, q, k, vt};
+    for (const void *p : ps) {
+        if (!p) return fail(kInvalid, "attn_ulysses_gather: NULL buffer");
+        if (!aligned(p, 16)) return fail(kInvalid, "attn_ulysses_gather: buffers must be 16-byte aligned");
+    }
+    return ok();
+}
+
+inline Check validate_ulysses_unpack(int n_ranks, int num_heads, int head_dim, int dt, int64_t rows,
+                                     const void *recv, const void *o) {
+    if (!dtype_known(dt)) return fail(kInvalid, "attn_ulysses_unpack_o: unknown dtype %d", dt);
+    if (n_ranks < 1 || num_heads < 1 || num_heads % n_ranks != 0)
+        return fail(kInvalid, "attn_ulysses_unpack_o: num_heads %d must be a positive multiple of n_ranks %d",
+                    num_heads, n_ranks);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "attn_ulysses_unpack_o: head_dim %d not supported for dtype %d", head_dim, dt);
+    if (rows < 0) return fail(kInvalid, "attn_ulysses_unpack_o: negative rows");
+    if (rows > kMaxTokens) return fail(kUnsupported, "attn_ulysses_unpack_o: rows above %lld", (long long)kMaxTokens);
+    if (rows == 0) return ok();
+    if (!recv || !o) return fail(kInvalid, "attn_ulysses_unpack_o: NULL buffer");
+    if (!aligned(recv, 16) || !aligned(o, 16))
+        return fail(kInvalid, "attn_ulysses_unpack_o: buffers must be 16-byte aligned");
+    return ok();
+}
+
 inline Check validate_merge(int n_parts, int num_heads, int head_dim, int64_t sq, const float *o_parts,
                             const float *lse_parts, const void *o_out, int out_dt, const float *lse_out) {
     if (n_parts < 1) return fail(kInvalid, "attn_merge_lse: n_parts %d < 1", n_parts);

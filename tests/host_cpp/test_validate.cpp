@@ -55,6 +55,21 @@ int main() {
     EXPECT(validate_partial(4, 64, kF16, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status ==
            kUnsupported);
     // merge
+    EXPECT(validate_shard(32, 8, 7).status == kOk);
+    EXPECT(validate_shard(32, 1, 0).status == kOk);
+    EXPECT(validate_shard(32, 3, 0).status == kInvalid);
+    EXPECT(validate_shard(32, 8, -1).status == kInvalid);
+    EXPECT(validate_shard(32, 0, 0).status == kInvalid);
+    EXPECT(validate_heads_forward(4, 128, kF16, P, P, P, 32768, P, 512, F).status == kOk);
+    EXPECT(validate_heads_forward(4, 128, kF16, P, P, P, 32768, P, 500, F).status == kInvalid);
+    EXPECT(validate_heads_forward(4, 64, kF32, P, P, P, 256, P, 256, nullptr).status == kOk);
+    EXPECT(validate_heads_forward(4, 128, kF16, P, P, P, kMaxTokens + 1, P, 512, F).status == kUnsupported);
+    EXPECT(validate_ulysses_gather(8, 4, 128, kF16, 32768, P, P, P, P, P, P).status == kOk);
+    EXPECT(validate_ulysses_gather(8, 4, 128, kF16, 32768 + 8, P, P, P, P, P, P).status == kInvalid);
+    EXPECT(validate_ulysses_gather(8, 4, 128, kF16, 8 * 12, P, P, P, P, P, P).status == kInvalid);
+    EXPECT(validate_ulysses_gather(8, 4, 128, kF16, 32768, P, nullptr, P, P, P, P).status == kInvalid);
+    EXPECT(validate_ulysses_unpack(8, 32, 128, kF16, 4096, P, P).status == kOk);
+    EXPECT(validate_ulysses_unpack(8, 36, 128, kF16, 4096, P, P).status == kInvalid);
     EXPECT(validate_set_prenorm(false, 1e-6f, false).status == kOk);
     EXPECT(validate_set_prenorm(false, 0.0f, false).status == kOk);
     EXPECT(validate_set_prenorm(true, 1e-6f, false).status == kInvalid);

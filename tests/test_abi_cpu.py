@@ -83,6 +83,33 @@ def test_set_prenorm_rejects_null_block(L):
     assert st == B.ATTN_E_INVALID_ARG and "blk is NULL" in _err(L)
 
 
+def test_shard_and_ulysses_reject(L):
+    h = ctypes.c_void_p()
+    st = L.attn_block_create_shard(ctypes.byref(h), 4096, 32, 3, 0, B.ATTN_F16, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == B.ATTN_E_INVALID_ARG and "n_ranks" in _err(L)
+    st = L.attn_block_create_shard(ctypes.byref(h), 4096, 32, 8, 8, B.ATTN_F16, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == B.ATTN_E_INVALID_ARG and "rank" in _err(L)
+    st = L.attn_block_create_shard(ctypes.byref(h), 4096, 32, 0, 0, B.ATTN_F16, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == B.ATTN_E_INVALID_ARG
+    assert h.value is None
+    # attn_heads_forward: o_ld too small, NULL, unsupported head_dim, seq 0
+    assert L.attn_heads_forward(4, 128, B.ATTN_F16, FAKE, FAKE, FAKE, 64, FAKE, 256, None, None) == B.ATTN_E_INVALID_ARG
+    assert L.attn_heads_forward(4, 128, B.ATTN_F16, None, FAKE, FAKE, 64, FAKE, 512, None, None) == B.ATTN_E_INVALID_ARG
+    assert L.attn_heads_forward(4, 64, B.ATTN_F16, FAKE, FAKE, FAKE, 64, FAKE, 512, None, None) == B.ATTN_E_UNSUPPORTED
+    assert L.attn_heads_forward(4, 128, B.ATTN_F16, FAKE, FAKE, FAKE, 0, FAKE, 512, None, None) == B.ATTN_OK
+    # Ulysses layouts: seq not n_ranks x multiple of 8, NULL, misaligned
+    g = lambda **kw: L.attn_ulysses_gather(kw.get("n", 8), 4, 128, B.ATTN_F16, kw.get("seq", 4096), FAKE, FAKE,
+                                           kw.get("rvt", FAKE), FAKE, FAKE, FAKE, None)
+    assert g(seq=4100) == B.ATTN_E_INVALID_ARG and "multiple of 8" in _err(L)
+    assert g(seq=8 * 12) == B.ATTN_E_INVALID_ARG
+    assert g(rvt=None) == B.ATTN_E_INVALID_ARG
+    assert g(rvt=FAKE + 8) == B.ATTN_E_INVALID_ARG
+    assert g(seq=0) == B.ATTN_OK
+    assert L.attn_ulysses_unpack_o(8, 30, 128, B.ATTN_F16, 16, FAKE, FAKE, None) == B.ATTN_E_INVALID_ARG
+    assert L.attn_ulysses_unpack_o(8, 32, 128, B.ATTN_F16, 16, None, FAKE, None) == B.ATTN_E_INVALID_ARG
+    assert L.attn_ulysses_unpack_o(8, 32, 128, B.ATTN_F16, 0, FAKE, FAKE, None) == B.ATTN_OK
+
+
 def test_partial_rejects(L):
     args = dict(nh=32, d=128, dt=B.ATTN_F16, q=FAKE, sq=256, qhs=256 * 128, k=FAKE, skv=512,
                 khs=512 * 128, v=FAKE, vhs=128 * 512, vrs=512, o=FAKE, lse=FAKE)
