@@ -326,6 +326,83 @@ def run_tp_share(torch, B, hip, warmup, steps, seq=8192, h=4096, nh=32, ranks=8,
         "share_tflops": sum(fl.values()) / (step["median"] * 1e-3) / 1e12,
     }
 
+def run_ring_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks=8, seed=0):
+    """Rank 0 of 8 with Ring-style streaming: its 4096-row query chunk against 8 K/V blocks of 4096 keys that
+    arrive by copy from pinned host memory (a stand-in for a peer's link) on the ring's copy stream while the
+    earlier blocks' attention runs. Reported beside the same work with K/V already resident (compute only) and
+    the copies alone (transfer only)."""
+    from long_context_self_amd.synthetic import block_inputs
+
+    d, ch = h // nh, seq // ranks
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=seed)
+    blk = B.AttnBlock(*(torch.from_numpy(w).cuda() for w in ws), num_heads=nh, max_tokens=seq)
+    q = torch.empty((nh, seq, d), dtype=torch.float16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.zeros((nh, d, B.vt_ld(seq)), dtype=torch.float16, device="cuda")
+    blk.forward(torch.from_numpy(x).cuda(), taps=B.Taps(q.data_ptr(), k.data_ptr(), vt.data_ptr(), None, None, 1,
+                                                           None))
+    torch.cuda.synchronize()
+    blk.close()
+    q0 = q[:, :ch].contiguous()
+    kd = [k[:, b * ch:(b + 1) * ch].contiguous() for b in range(ranks)]
+    vd = [vt[:, :, b * ch:(b + 1) * ch].contiguous() for b in range(ranks)]
+    kh = [t.cpu().pin_memory() for t in kd]
+    vh = [t.cpu().pin_memory() for t in vd]
+    del q, k, vt
+    lens = [ch] * ranks
+    ring = B.AttnRing(nh, d, ranks, ch, ch)
+    o = torch.empty((ch, h), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    slot = [torch.empty_like(kd[0]), torch.empty_like(vd[0])]
+
+    def timed(fn):
+        evs = hip.events(2 * steps)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        for s_ in range(steps):
+            hip.record(evs[2 * s_], stream)
+            fn()
+            hip.record(evs[2 * s_ + 1], stream)
+        torch.cuda.synchronize()
+        r = stats([hip.ms(evs[2 * s_], evs[2 * s_ + 1]) for s_ in range(steps)])
+        hip.destroy(evs)
+        return r
+
+    t_host = timed(lambda: ring.forward(q0, ch, kh, vh, lens, o))
+    t_dev = timed(lambda: ring.forward(q0, ch, kd, vd, lens, o))
+
+    def copies():
+        for b in range(ranks):
+            slot[0].copy_(kh[b], non_blocking=True)
+            slot[1].copy_(vh[b], non_blocking=True)
+
+    t_copy = timed(copies)
+    o_parts = torch.empty((ranks, nh, ch, d), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((ranks, nh, ch), dtype=torch.float32, device="cuda")
+
+    def compute():
+        for b in range(ranks):
+            B.attn_partial_forward(nh, d, q0, ch, ch * d, kd[b], ch, ch * d, vd[b], d * ch, ch, o_parts[b],
+                                   lse_parts[b])
+        B.attn_merge_lse(ranks, nh, d, ch, o_parts, lse_parts, o, torch.float16)
+
+    t_comp = timed(compute)
+    ring.close()
+    kv_bytes = 2 * ranks * nh * ch * d * 2
+    tc, tx, tr = t_comp["median"], t_copy["median"], t_host["median"]
+    del kd, vd, kh, vh, q0, o, o_parts, lse_parts, slot
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"ring streaming: rank 0 of {ranks} at seq {seq} (query chunk {ch}) vs {ranks} K/V blocks of {ch} "
+                    f"keys copied from pinned host memory while earlier blocks compute, hidden {h}",
+        "ms": tr, "ring_host_blocks_ms": t_host, "ring_device_blocks_ms": t_dev,
+        "compute_only_ms": t_comp, "transfer_only_ms": t_copy,
+        "transfer_gbs": kv_bytes / (tx * 1e-3) / 1e9,
+        "overlap_efficiency": (tc + tx - tr) / min(tc, tx),
+        "attention_tflops_device_blocks": 4.0 * ch * seq * h / (t_dev["median"] * 1e-3) / 1e12,
+    }
+
 COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_counters_seq8192_h4096.txt")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_self_amd", "csrc")
 
@@ -494,6 +571,11 @@ def main() -> int:
         log("tensor-parallel share (rank 0 of 8), seq 8192")
         extra.append(run_tp_share(torch, B, hip, w, st))
         log(f"  {extra[-1]['ms_per_forward']:.3f} ms/forward, {extra[-1]['share_tflops']:.0f} TFLOP/s")
+        log("ring streaming (rank 0 of 8), seq 32768, K/V blocks from pinned host memory")
+        extra.append(run_ring_share(torch, B, hip, w, st))
+        log(f"  {extra[-1]['ms']:.3f} ms (compute only {extra[-1]['compute_only_ms']['median']:.3f}, transfer only "
+            f"{extra[-1]['transfer_only_ms']['median']:.3f} at {extra[-1]['transfer_gbs']:.0f} GB/s), overlap "
+            f"efficiency {extra[-1]['overlap_efficiency']:.2f}")
         log("6 stacked blocks seq 32768")
         m6, k6 = run_block(torch, B, hip, 32768, 4096, 32, 6, 1, 3)
         f6 = block_flops(32768, 4096)

@@ -278,6 +278,51 @@ attn_status_t attn_merge_lse(int n_parts, int num_heads, int head_dim, int64_t s
                              void *o_out, attn_dtype_t out_dt, float *lse_out,
                              hipStream_t stream);
 
+/*
+ * attn_ring_t -- Ring-style streaming of K/V blocks on one GPU. K/V blocks
+ * arrive by asynchronous copy on the ring's own copy stream while the
+ * attention of the blocks already in place runs on the caller's stream; the
+ * per-block partial results are merged by log-sum-exp. [Ring Attention:
+ * K/V streamed around the GPUs, local Q computation overlapped with the
+ * transfer, blocks combined by online softmax, the full K/V never resident --
+ * news summary of "Scaling AI Inference Across Multiple GPUs Using NVIDIA
+ * TensorRT with Multi-Device Inference Support", the three context-parallel
+ * implementations.]
+ *
+ * attn_ring_create -- allocate two staging slots (K [H][max_block_len][d] and
+ * V^T [H][d][ATTN_VT_LD(max_block_len)]), n_blocks partial results for up to
+ * max_sq query rows (fp32, about n_blocks*H*max_sq*d*4 bytes), a copy stream
+ * (default priority) and its events. Errors: ATTN_E_INVALID_ARG,
+ * ATTN_E_UNSUPPORTED (head_dim, dtype, sizes), ATTN_E_OOM, ATTN_E_HIP.
+ */
+typedef struct attn_ring attn_ring_t;
+attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, attn_dtype_t dt, int n_blocks,
+                               int64_t max_sq, int64_t max_block_len);
+
+/*
+ * attn_ring_forward -- o = softmax(q_scaled K^T) V over the keys of all
+ * n_blocks blocks, for sq query rows, all heads.
+ *   q_scaled    device [H][sq][d] (times 1/sqrt(d)), 16-byte aligned.
+ *   k_blocks[b] [H][len_b][d] and vt_blocks[b] [H][d][ATTN_VT_LD(len_b)]:
+ *               block b as its owner holds it (e.g. the taps of its
+ *               projection); device memory or pinned host memory (a
+ *               stand-in for a peer's link). Host arrays of n_blocks entries.
+ *   block_lens  host array, 0 <= len_b <= max_block_len (0: an empty block).
+ *   o_out       device [sq][H*d] token-major in dt; lse_out NULL or fp32 [H][sq].
+ * Block b is copied into slot b % 2 on the copy stream once block b-2's
+ * partial has finished on `stream`, so the copy of block b+1 overlaps the
+ * partial of block b; `stream` waits for each block's arrival. The copies of
+ * a call start after the work already enqueued on `stream`; calls on one ring
+ * must use one stream (or be ordered by the caller). The result equals
+ * attn_partial_forward over each block followed by attn_merge_lse.
+ */
+attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled, int64_t sq,
+                                const void *const *k_blocks, const void *const *vt_blocks,
+                                const int64_t *block_lens, void *o_out, float *lse_out, hipStream_t stream);
+
+/* attn_ring_destroy -- synchronise the ring's device and free it. NULL is a no-op. */
+void attn_ring_destroy(attn_ring_t *ring);
+
 /* attn_block_destroy -- synchronise the block's device and free everything
  * the block owns. NULL is a no-op. */
 void attn_block_destroy(attn_block_t *blk);

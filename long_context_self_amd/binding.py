@@ -8,7 +8,8 @@ unless one is passed). The functions keep the C names:
   ``attn_block_destroy`` (wrapped by the ``AttnBlock`` class),
 * ``attn_block_create_shard`` (tensor-parallel share, ``AttnBlock(..., n_ranks=, rank=)``),
 * ``attn_partial_forward``, ``attn_merge_lse``, ``attn_heads_forward``,
-* ``attn_ulysses_gather``, ``attn_ulysses_unpack_o``.
+* ``attn_ulysses_gather``, ``attn_ulysses_unpack_o``,
+* ``attn_ring_create`` / ``attn_ring_forward`` / ``attn_ring_destroy`` (the ``AttnRing`` class).
 
 There is no fallback: if the library is missing or fails to load, ``lib()``
 raises, and every call raises ``AttnError`` on a non-OK status.
@@ -30,7 +31,8 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_E_INVALID_ARG", 2: "ATTN_E_UNSUPPORTED", 
 
 EXPORTS = ("attn_block_create", "attn_block_create_shard", "attn_block_set_prenorm", "attn_block_forward",
            "attn_partial_forward", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
-           "attn_ulysses_unpack_o", "attn_block_destroy", "attn_last_error")
+           "attn_ulysses_unpack_o", "attn_ring_create", "attn_ring_forward", "attn_ring_destroy",
+           "attn_block_destroy", "attn_last_error")
 
 
 def vt_ld(seq: int) -> int:
@@ -72,6 +74,13 @@ def lib() -> ctypes.CDLL:
     L.attn_ulysses_gather.restype = i32
     L.attn_ulysses_unpack_o.argtypes = [i32, i32, i32, i32, i64, vp, vp, vp]
     L.attn_ulysses_unpack_o.restype = i32
+    L.attn_ring_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, i64, i64]
+    L.attn_ring_create.restype = i32
+    L.attn_ring_forward.argtypes = [vp, vp, i64, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64), vp, vp,
+                                    vp]
+    L.attn_ring_forward.restype = i32
+    L.attn_ring_destroy.argtypes = [vp]
+    L.attn_ring_destroy.restype = None
     L.attn_block_set_prenorm.argtypes = [vp, vp, ctypes.c_float, vp]
     L.attn_block_set_prenorm.restype = i32
     L.attn_block_forward.argtypes = [vp, vp, vp, i64, i64, ctypes.POINTER(Taps), vp]
@@ -179,6 +188,39 @@ def attn_merge_lse(n_parts: int, num_heads: int, head_dim: int, sq: int, o_parts
                    out_dtype: torch.dtype = torch.float16, lse_out=None, stream=None) -> None:
     _check(lib().attn_merge_lse(n_parts, num_heads, head_dim, sq, _ptr(o_parts), _ptr(lse_parts),
                                 _ptr(o_out), _dtype_code(out_dtype), _ptr(lse_out), _stream(stream)))
+
+
+class AttnRing:
+    """Ring-style K/V streaming (attn_ring_*): blocks copied on the ring's copy
+    stream while earlier blocks' attention runs, merged by log-sum-exp."""
+
+    def __init__(self, num_heads: int, head_dim: int, n_blocks: int, max_sq: int, max_block_len: int,
+                 dtype: torch.dtype = torch.float16):
+        self.n_blocks = n_blocks
+        self.dtype = dtype
+        handle = ctypes.c_void_p()
+        _check(lib().attn_ring_create(ctypes.byref(handle), num_heads, head_dim, _dtype_code(dtype), n_blocks,
+                                      max_sq, max_block_len))
+        self.handle = handle.value
+
+    def forward(self, q_scaled, sq: int, k_blocks, vt_blocks, block_lens, o_out, lse_out=None, stream=None) -> None:
+        n = self.n_blocks
+        kb = (ctypes.c_void_p * n)(*[_ptr(t) for t in k_blocks])
+        vb = (ctypes.c_void_p * n)(*[_ptr(t) for t in vt_blocks])
+        lens = (ctypes.c_int64 * n)(*block_lens)
+        _check(lib().attn_ring_forward(self.handle, _ptr(q_scaled), sq, kb, vb, lens, _ptr(o_out), _ptr(lse_out),
+                                       _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib().attn_ring_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class AttnBlock:

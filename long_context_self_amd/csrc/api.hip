@@ -8,9 +8,8 @@
 #include "attn_block.h"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "status.hpp"
 #include "validate.hpp"
-
-#define ATTN_API extern "C" __attribute__((visibility("default")))
 
 using namespace attnblk;
 
@@ -32,30 +31,6 @@ struct attn_block {
 
 namespace {
 
-thread_local char g_last_error[512] = "";
-
-attn_status_t set_error(int status, const char *msg) {
-    std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
-    return static_cast<attn_status_t>(status);
-}
-
-attn_status_t report(const Check &c) {
-    if (c.status == kOk) return ATTN_OK;
-    return set_error(c.status, c.msg);
-}
-
-attn_status_t hip_fail(const char *where, hipError_t e) {
-    char buf[512];
-    std::snprintf(buf, sizeof(buf), "%s: %s", where, hipGetErrorString(e));
-    return set_error(kHip, buf);
-}
-
-#define HIP_TRY(where, expr)                            \
-    do {                                                \
-        hipError_t e_ = (expr);                         \
-        if (e_ != hipSuccess) return hip_fail(where, e_); \
-    } while (0)
-
 void free_block(attn_block *b) {
     if (!b) return;
     void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o, b->ws_rs};
@@ -66,7 +41,7 @@ void free_block(attn_block *b) {
 
 }  // namespace
 
-ATTN_API const char *attn_last_error(void) { return g_last_error; }
+ATTN_API const char *attn_last_error(void) { return last_error_buffer(); }
 
 namespace {
 

@@ -76,6 +76,7 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &g, half_t *st, int m
 
 __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM_BYTES];
+    __shared__ float rs_tile[BM];  // RMSNorm row factors of the tile's rows (pre-norm only)
     half_t *smem = reinterpret_cast<half_t *>(smem_raw);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     const int tm = first_m + (w % per_group) % gsize;
     const int tn = (w % per_group) / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
+    // published to every wave by the barriers of the main loop
+    if (g.row_scale && tid < BM) rs_tile[tid] = g.row_scale[min(m0 + tid, g.M - 1)];
     const bool edge = (m0 + BM > g.M) || (n0 + BN > g.N);
 
     floatx16 acc[4][2];
@@ -190,11 +193,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const int row = wm * 128 + i * 32 + 8 * gg + 4 * h;
-                // RMSNorm pre-norm: output row m scales by 1 / rms(x_m) (rows past M clamp)
+                // RMSNorm pre-norm: output row m scales by 1 / rms(x_m)
                 float rsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
                 if (g.row_scale) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) rsc[r] = g.row_scale[min(m0 + row + r, g.M - 1)];
+                    for (int r = 0; r < 4; ++r) rsc[r] = rs_tile[row + r];
                 }
                 if (v_tile) {
                     half4 v;

@@ -1,0 +1,191 @@
+// Ring-style streaming of K/V blocks on one GPU: the blocks arrive by
+// asynchronous copy on a copy stream while the attention of earlier blocks
+// runs on the caller's stream, and the per-block partial results are merged
+// by log-sum-exp at the end. This is the pattern of Ring Attention -- K/V
+// streamed around the ranks, each rank overlapping its local Q computation
+// with the transfer and combining the blocks by online softmax, never
+// holding the full K/V (news summary of "Scaling AI Inference Across Multiple
+// GPUs Using NVIDIA TensorRT with Multi-Device Inference Support", the three
+// context-parallel implementations).
+//
+// Schedule, for block b in slot b % 2 of a two-slot staging buffer:
+//   copy stream:    [wait freed[b%2]] copy K_b, V_b -> slot; record arrived[b%2]
+//   compute stream: wait arrived[b%2]; partial(Q, slot) -> (O_b, LSE_b); record freed[b%2]
+// so the copy of block b+1 runs while block b's partial computes, and no copy
+// overwrites a slot whose previous block is still being read. The sources
+// may be device memory or pinned host memory (hipMemcpyAsync with
+// hipMemcpyDefault), standing in for a peer's link.
+
+#include <cstring>
+
+#include "attn_block.h"
+#include "common.hpp"
+#include "kernels.hpp"
+#include "status.hpp"
+#include "validate.hpp"
+
+using namespace attnblk;
+
+struct attn_ring {
+    int heads, head_dim, dt, n_blocks, device;
+    int64_t max_sq, max_block;
+    void *slot_k[2], *slot_vt[2];  // K [H][len][d], V^T [H][d][ATTN_VT_LD(len)] of the block in the slot
+    float *o_parts;                // [n_blocks][H][max_sq][d] (each block's part packed for the sq of a call)
+    float *lse_parts;              // [n_blocks][H][max_sq]
+    hipStream_t copy;
+    hipEvent_t start, arrived[2], freed[2];
+};
+
+namespace {
+
+void free_ring(attn_ring *r) {
+    if (!r) return;
+    void *ptrs[] = {r->slot_k[0], r->slot_k[1], r->slot_vt[0], r->slot_vt[1], r->o_parts, r->lse_parts};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    hipEvent_t evs[] = {r->start, r->arrived[0], r->arrived[1], r->freed[0], r->freed[1]};
+    for (hipEvent_t e : evs)
+        if (e) (void)hipEventDestroy(e);
+    if (r->copy) (void)hipStreamDestroy(r->copy);
+    delete r;
+}
+
+}  // namespace
+
+ATTN_API attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, attn_dtype_t dt,
+                                        int n_blocks, int64_t max_sq, int64_t max_block_len) {
+    Check c = validate_ring_create(out == nullptr, num_heads, head_dim, (int)dt, n_blocks, max_sq, max_block_len);
+    if (c.status != kOk) {
+        if (out) *out = nullptr;
+        return report(c);
+    }
+    *out = nullptr;
+    attn_ring *r = new (std::nothrow) attn_ring();
+    if (!r) return set_error(kOom, "attn_ring_create: host allocation failed");
+    std::memset(r, 0, sizeof(*r));
+    r->heads = num_heads;
+    r->head_dim = head_dim;
+    r->dt = (int)dt;
+    r->n_blocks = n_blocks;
+    r->max_sq = max_sq;
+    r->max_block = max_block_len;
+    hipError_t e = hipGetDevice(&r->device);
+    const size_t es = elem_size(r->dt), hd = (size_t)num_heads * head_dim;
+    struct {
+        void **p;
+        size_t bytes;
+    } allocs[] = {{&r->slot_k[0], hd * max_block_len * es},
+                  {&r->slot_k[1], hd * max_block_len * es},
+                  {&r->slot_vt[0], hd * ATTN_VT_LD(max_block_len) * es},
+                  {&r->slot_vt[1], hd * ATTN_VT_LD(max_block_len) * es},
+                  {reinterpret_cast<void **>(&r->o_parts), (size_t)n_blocks * hd * max_sq * sizeof(float)},
+                  {reinterpret_cast<void **>(&r->lse_parts), (size_t)n_blocks * num_heads * max_sq * sizeof(float)}};
+    for (auto &a : allocs) {
+        if (e != hipSuccess) break;
+        e = hipMalloc(a.p, a.bytes);
+        if (e != hipSuccess) {
+            *a.p = nullptr;
+            free_ring(r);
+            (void)hipGetLastError();
+            return set_error(kOom, "attn_ring_create: device allocation failed");
+        }
+    }
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->copy, hipStreamNonBlocking);
+    hipEvent_t *evs[] = {&r->start, &r->arrived[0], &r->arrived[1], &r->freed[0], &r->freed[1]};
+    for (hipEvent_t *ev : evs)
+        if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        free_ring(r);
+        return hip_fail("attn_ring_create", e);
+    }
+    *out = r;
+    return ATTN_OK;
+}
+
+ATTN_API void attn_ring_destroy(attn_ring_t *ring) {
+    if (!ring) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(ring->device);
+    (void)hipDeviceSynchronize();
+    free_ring(ring);
+    (void)hipSetDevice(cur);
+}
+
+ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled, int64_t sq,
+                                         const void *const *k_blocks, const void *const *vt_blocks,
+                                         const int64_t *block_lens, void *o_out, float *lse_out,
+                                         hipStream_t stream) {
+    Check c = validate_ring_forward(ring == nullptr, ring ? ring->n_blocks : 0, ring ? ring->max_sq : 0,
+                                    ring ? ring->max_block : 0, q_scaled, sq, k_blocks, vt_blocks, block_lens,
+                                    o_out, lse_out);
+    if (c.status != kOk) return report(c);
+    if (sq == 0) return ATTN_OK;
+    const int H = ring->heads, d = ring->head_dim, nb = ring->n_blocks;
+    const size_t es = elem_size(ring->dt);
+    // copies of this call start after the work already on `stream` (q, the caller's
+    // buffers, and an earlier call's use of the slots)
+    HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->start, stream));
+    HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(ring->copy, ring->start, 0));
+    for (int b = 0; b < nb; ++b) {
+        const int slot = b & 1;
+        const int64_t len = block_lens[b];
+        const int64_t ld = ATTN_VT_LD(len);
+        if (b >= 2) HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(ring->copy, ring->freed[slot], 0));
+        if (len > 0) {
+            HIP_TRY("attn_ring_forward: K copy", hipMemcpyAsync(ring->slot_k[slot], k_blocks[b], (size_t)H * len * d * es,
+                                                                hipMemcpyDefault, ring->copy));
+            HIP_TRY("attn_ring_forward: V copy", hipMemcpyAsync(ring->slot_vt[slot], vt_blocks[b],
+                                                                (size_t)H * d * ld * es, hipMemcpyDefault, ring->copy));
+        }
+        HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->arrived[slot], ring->copy));
+        HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(stream, ring->arrived[slot], 0));
+        float *ob = ring->o_parts + (size_t)b * H * sq * d;
+        float *lb = ring->lse_parts + (size_t)b * H * sq;
+        if (ring->dt == kF16) {
+            FlashArgs fa{};
+            fa.q = static_cast<const _Float16 *>(q_scaled);
+            fa.k = static_cast<const _Float16 *>(ring->slot_k[slot]);
+            fa.vt = static_cast<const _Float16 *>(ring->slot_vt[slot]);
+            fa.q_head_stride = sq * d;
+            fa.k_head_stride = len * d;
+            fa.v_head_stride = (int64_t)d * ld;
+            fa.v_row_stride = ld;
+            fa.sq = (int)sq;
+            fa.skv = (int)len;
+            fa.num_heads = H;
+            fa.o32 = ob;
+            fa.lse = lb;
+            HIP_TRY("attn_ring_forward: partial", launch_flash_fwd_f16(fa, stream));
+        } else {
+            FlashArgsF32 fa{};
+            fa.q = static_cast<const float *>(q_scaled);
+            fa.k = static_cast<const float *>(ring->slot_k[slot]);
+            fa.vt = static_cast<const float *>(ring->slot_vt[slot]);
+            fa.q_head_stride = sq * d;
+            fa.k_head_stride = len * d;
+            fa.v_head_stride = (int64_t)d * ld;
+            fa.v_row_stride = ld;
+            fa.sq = (int)sq;
+            fa.skv = (int)len;
+            fa.num_heads = H;
+            fa.head_dim = d;
+            fa.o32 = ob;
+            fa.lse = lb;
+            HIP_TRY("attn_ring_forward: partial", launch_flash_fwd_f32(fa, stream));
+        }
+        HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->freed[slot], stream));
+    }
+    MergeArgs m{};
+    m.n_parts = nb;
+    m.num_heads = H;
+    m.head_dim = d;
+    m.sq = sq;
+    m.o_parts = ring->o_parts;
+    m.lse_parts = ring->lse_parts;
+    m.o_out = o_out;
+    m.out_f16 = ring->dt == kF16;
+    m.lse_out = lse_out;
+    HIP_TRY("attn_ring_forward: merge", launch_lse_merge(m, stream));
+    return ATTN_OK;
+}

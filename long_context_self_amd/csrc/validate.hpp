@@ -220,6 +220,40 @@ inline Check validate_ulysses_unpack(int n_ranks, int num_heads, int head_dim, i
     return ok();
 }
 
+inline Check validate_ring_create(bool out_null, int num_heads, int head_dim, int dt, int n_blocks, int64_t max_sq,
+                                  int64_t max_block) {
+    if (out_null) return fail(kInvalid, "attn_ring_create: out is NULL");
+    if (!dtype_known(dt)) return fail(kInvalid, "attn_ring_create: unknown dtype %d", dt);
+    if (num_heads < 1) return fail(kInvalid, "attn_ring_create: num_heads %d < 1", num_heads);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "attn_ring_create: head_dim %d not supported for dtype %d", head_dim, dt);
+    if (n_blocks < 1) return fail(kInvalid, "attn_ring_create: n_blocks %d < 1", n_blocks);
+    if (n_blocks > kMaxParts) return fail(kUnsupported, "attn_ring_create: n_blocks %d > %d", n_blocks, kMaxParts);
+    if (max_sq < 1 || max_block < 1) return fail(kInvalid, "attn_ring_create: max_sq and max_block_len must be >= 1");
+    if (max_sq > kMaxTokens || max_block > kMaxTokens)
+        return fail(kUnsupported, "attn_ring_create: max_sq or max_block_len above %lld", (long long)kMaxTokens);
+    return ok();
+}
+
+inline Check validate_ring_forward(bool ring_null, int n_blocks, int64_t max_sq, int64_t max_block, const void *q,
+                                   int64_t sq, const void *const *kb, const void *const *vb, const int64_t *lens,
+                                   const void *o, const float *lse) {
+    if (ring_null) return fail(kInvalid, "attn_ring_forward: ring is NULL");
+    if (sq < 0 || sq > max_sq) return fail(kInvalid, "attn_ring_forward: sq %lld outside [0, %lld]", (long long)sq,
+                                           (long long)max_sq);
+    if (sq == 0) return ok();
+    if (!q || !o || !kb || !vb || !lens) return fail(kInvalid, "attn_ring_forward: NULL argument");
+    if (!aligned(q, 16) || !aligned(o, 16)) return fail(kInvalid, "attn_ring_forward: q and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(kInvalid, "attn_ring_forward: lse misaligned");
+    for (int b = 0; b < n_blocks; ++b) {
+        if (lens[b] < 0 || lens[b] > max_block)
+            return fail(kInvalid, "attn_ring_forward: block %d length %lld outside [0, %lld]", b, (long long)lens[b],
+                        (long long)max_block);
+        if (lens[b] > 0 && (!kb[b] || !vb[b])) return fail(kInvalid, "attn_ring_forward: block %d K or V^T is NULL", b);
+    }
+    return ok();
+}
+
 inline Check validate_merge(int n_parts, int num_heads, int head_dim, int64_t sq, const float *o_parts,
                             const float *lse_parts, const void *o_out, int out_dt, const float *lse_out) {
     if (n_parts < 1) return fail(kInvalid, "attn_merge_lse: n_parts %d < 1", n_parts);

@@ -70,6 +70,21 @@ int main() {
     EXPECT(validate_ulysses_gather(8, 4, 128, kF16, 32768, P, nullptr, P, P, P, P).status == kInvalid);
     EXPECT(validate_ulysses_unpack(8, 32, 128, kF16, 4096, P, P).status == kOk);
     EXPECT(validate_ulysses_unpack(8, 36, 128, kF16, 4096, P, P).status == kInvalid);
+    EXPECT(validate_ring_create(false, 32, 128, kF16, 8, 4096, 4096).status == kOk);
+    EXPECT(validate_ring_create(true, 32, 128, kF16, 8, 4096, 4096).status == kInvalid);
+    EXPECT(validate_ring_create(false, 32, 128, kF16, kMaxParts + 1, 4096, 4096).status == kUnsupported);
+    EXPECT(validate_ring_create(false, 32, 128, kF16, 8, 4096, kMaxTokens + 1).status == kUnsupported);
+    {
+        const void *kb[3] = {P, P, nullptr};
+        const int64_t lens_ok[3] = {64, 100, 0}, lens_big[3] = {64, 5000, 0}, lens_null[3] = {64, 100, 8};
+        EXPECT(validate_ring_forward(false, 3, 4096, 4096, P, 300, kb, kb, lens_ok, P, F).status == kOk);
+        EXPECT(validate_ring_forward(false, 3, 4096, 4096, P, 300, kb, kb, lens_big, P, F).status == kInvalid);
+        EXPECT(validate_ring_forward(false, 3, 4096, 4096, P, 300, kb, kb, lens_null, P, F).status == kInvalid);
+        EXPECT(validate_ring_forward(false, 3, 4096, 4096, P, 5000, kb, kb, lens_ok, P, F).status == kInvalid);
+        EXPECT(validate_ring_forward(true, 3, 4096, 4096, P, 300, kb, kb, lens_ok, P, F).status == kInvalid);
+        EXPECT(validate_ring_forward(false, 3, 4096, 4096, P, 0, nullptr, nullptr, nullptr, nullptr, nullptr).status ==
+               kOk);
+    }
     EXPECT(validate_set_prenorm(false, 1e-6f, false).status == kOk);
     EXPECT(validate_set_prenorm(false, 0.0f, false).status == kOk);
     EXPECT(validate_set_prenorm(true, 1e-6f, false).status == kInvalid);

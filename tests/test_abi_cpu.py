@@ -110,6 +110,18 @@ def test_shard_and_ulysses_reject(L):
     assert L.attn_ulysses_unpack_o(8, 32, 128, B.ATTN_F16, 0, FAKE, FAKE, None) == B.ATTN_OK
 
 
+def test_ring_rejects(L):
+    h = ctypes.c_void_p()
+    assert L.attn_ring_create(None, 32, 128, B.ATTN_F16, 8, 4096, 4096) == B.ATTN_E_INVALID_ARG
+    assert L.attn_ring_create(ctypes.byref(h), 32, 64, B.ATTN_F16, 8, 4096, 4096) == B.ATTN_E_UNSUPPORTED
+    assert L.attn_ring_create(ctypes.byref(h), 32, 128, B.ATTN_F16, 0, 4096, 4096) == B.ATTN_E_INVALID_ARG
+    assert L.attn_ring_create(ctypes.byref(h), 32, 128, B.ATTN_F16, 8, 0, 4096) == B.ATTN_E_INVALID_ARG
+    assert h.value is None
+    assert L.attn_ring_forward(None, FAKE, 16, None, None, None, FAKE, None, None) == B.ATTN_E_INVALID_ARG
+    assert "ring is NULL" in _err(L)
+    L.attn_ring_destroy(None)
+
+
 def test_partial_rejects(L):
     args = dict(nh=32, d=128, dt=B.ATTN_F16, q=FAKE, sq=256, qhs=256 * 128, k=FAKE, skv=512,
                 khs=512 * 128, v=FAKE, vhs=128 * 512, vrs=512, o=FAKE, lse=FAKE)
