@@ -24,6 +24,8 @@ struct attn_block {
     void *w_qkv;  // fp16: [3*width][hidden] = [W_Q|W_K|W_V]^T (this shard's columns); fp32: [hidden][3*width]
     void *w_o;    // fp16: [hidden][width] = W_O^T (this shard's rows);              fp32: [width][hidden]
     void *ws_q, *ws_k, *ws_vt, *ws_o;
+    float *ws_split_o;    // [kMaxSplit][heads][max_tokens][head_dim] fp32 key-split partials (small grids only)
+    float *ws_split_lse;  // [kMaxSplit][heads][max_tokens]
     int prenorm;      // RMSNorm of the input enabled (gain folded into w_qkv)
     float norm_eps;
     float *ws_rs;     // [max_tokens] per-row 1 / rms(x), when prenorm
@@ -33,7 +35,7 @@ namespace {
 
 void free_block(attn_block *b) {
     if (!b) return;
-    void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o, b->ws_rs};
+    void *ptrs[] = {b->w_qkv, b->w_o, b->ws_q, b->ws_k, b->ws_vt, b->ws_o, b->ws_rs, b->ws_split_o, b->ws_split_lse};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete b;
@@ -44,6 +46,25 @@ void free_block(attn_block *b) {
 ATTN_API const char *attn_last_error(void) { return last_error_buffer(); }
 
 namespace {
+
+// Attention launches with fewer workgroups than this leave CUs idle (one
+// 512-thread workgroup per CU, 256 CUs): the keys are then split into up to
+// kMaxSplit ranges whose partials are merged by LSE.
+constexpr int kFillWorkgroups = 512;
+constexpr int kMaxSplit = 4;
+constexpr int kFlashRows = 256;  // query rows per attention workgroup
+
+int64_t attn_workgroups(int heads, int64_t seq) { return heads * ((seq + kFlashRows - 1) / kFlashRows); }
+
+// Number of key ranges for an attention over `seq` keys of `heads` heads, and
+// the keys per range (a multiple of 64, the kernel's tile).
+int split_keys(int heads, int64_t seq, int &len) {
+    const int64_t wgs = attn_workgroups(heads, seq);
+    int n = 1;
+    while (n < kMaxSplit && wgs * n < kFillWorkgroups && seq >= 512 * (int64_t)(n + 1)) ++n;
+    len = (int)(((seq + n - 1) / n + 63) / 64 * 64);
+    return (int)((seq + len - 1) / len);
+}
 
 // Pack the weight shard of `rank` (heads [rank*H/N, (rank+1)*H/N): columns
 // [c0, c0+width) of W_Q, W_K, W_V and rows [c0, c0+width) of W_O) and
@@ -81,6 +102,18 @@ attn_status_t create_block(attn_block_t **out, int hidden, int num_heads, int n_
         e = hipMalloc(a.p, a.bytes);
         if (e != hipSuccess) {
             *a.p = nullptr;
+            free_block(b);
+            (void)hipGetLastError();
+            return set_error(kOom, "attn_block_create: device allocation failed");
+        }
+    }
+    if (b->dt == kF16 && attn_workgroups(b->heads, max_tokens) < 2 * kFillWorkgroups) {
+        // small grids possible: key-split partials
+        e = hipMalloc(reinterpret_cast<void **>(&b->ws_split_o), (size_t)kMaxSplit * qk_bytes / es * sizeof(float));
+        if (e == hipSuccess)
+            e = hipMalloc(reinterpret_cast<void **>(&b->ws_split_lse),
+                          (size_t)kMaxSplit * b->heads * max_tokens * sizeof(float));
+        if (e != hipSuccess) {
             free_block(b);
             (void)hipGetLastError();
             return set_error(kOom, "attn_block_create: device allocation failed");
@@ -232,10 +265,33 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         fa.sq = S;
         fa.skv = S;
         fa.num_heads = H;
-        fa.o16 = static_cast<_Float16 *>(o);
-        fa.o16_ld = wd;
-        fa.lse = lse;
-        HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
+        int split_len = 0;
+        const int n_split = blk->ws_split_o ? split_keys(H, S, split_len) : 1;
+        if (n_split > 1) {
+            // few workgroups: partials over key ranges, then the LSE merge writes o (and lse)
+            fa.n_split = n_split;
+            fa.split_len = split_len;
+            fa.o32 = blk->ws_split_o;
+            fa.lse = blk->ws_split_lse;
+            HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
+            MergeArgs m{};
+            m.n_parts = n_split;
+            m.num_heads = H;
+            m.head_dim = d;
+            m.sq = S;
+            m.o_parts = blk->ws_split_o;
+            m.lse_parts = blk->ws_split_lse;
+            m.o_out = o;
+            m.o_ld = wd;
+            m.out_f16 = 1;
+            m.lse_out = lse;
+            HIP_TRY("attn_block_forward: attention merge", launch_lse_merge(m, stream));
+        } else {
+            fa.o16 = static_cast<_Float16 *>(o);
+            fa.o16_ld = wd;
+            fa.lse = lse;
+            HIP_TRY("attn_block_forward: attention", launch_flash_fwd_f16(fa, stream));
+        }
         MARK(2);
         GemmArgs go{};
         go.a = static_cast<const _Float16 *>(o);

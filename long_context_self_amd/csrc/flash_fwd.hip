@@ -352,8 +352,14 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 
     const int nqb = (a.sq + BQ - 1) / BQ;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = work / nqb;
-    const int qb = work % nqb;
+    const int per_split = nqb * a.num_heads;
+    const int split = a.n_split > 1 ? work / per_split : 0;
+    const int head = (work - split * per_split) / nqb;
+    const int qb = (work - split * per_split) % nqb;
+    const int key_base = split * a.split_len;
+    const int skv = a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
+    float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
+    float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
 
     const half_t *qh = a.q + (int64_t)head * a.q_head_stride;
     const int q = qb * BQ + wave * 32 + (lane & 31);
@@ -368,15 +374,15 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     Ctx c;
-    c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride);
-    c.vh = reinterpret_cast<const char *>(a.vt + (int64_t)head * a.v_head_stride);
+    c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D);
+    c.vh = reinterpret_cast<const char *>(a.vt + (int64_t)head * a.v_head_stride + key_base);
     c.ring = smem;
     c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
     c.lo = load_offsets(a, wave, lane);
     c.wave = wave;
     c.lane = lane;
-    c.skv = a.skv;
-    c.T = (a.skv + BN - 1) / BN;
+    c.skv = skv;
+    c.T = (skv + BN - 1) / BN;
     c.vrs = a.v_row_stride;
     const int T = c.T;
 
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
                 sa[kb] = mfma32(fa[n], qf[kk], kk == 0 ? floatx16{} : sa[kb]);
             }
         }
-        const float mt = (BN <= a.skv) ? row_max<false>(sa, 0, a.skv, h) : row_max<true>(sa, 0, a.skv, h);
+        const float mt = (BN <= skv) ? row_max<false>(sa, 0, skv, h) : row_max<true>(sa, 0, skv, h);
         update_max(mt, m_run, l_run, o);
         // Step 0 refills slot 3: every wave must be done reading K_0.
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 
         // Steady steps need stage t+3 full (t + 4 <= last full tile) and run
         // in pairs, so the two S register sets swap roles without copies.
-        const int last_full = (a.skv % BN == 0) ? T - 1 : T - 2;
+        const int last_full = (skv % BN == 0) ? T - 1 : T - 2;
         const int n_steady = max(0, last_full - 3);
         int t = 0;
         if (n_steady >= 2) {
@@ -426,14 +432,14 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     // ---- epilogue: combine the two lane halves' sums, normalise, stage the
     // wave's 32 x 128 block through LDS and store whole rows.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const bool empty = a.skv == 0;
+    const bool empty = skv == 0;
     const float inv = empty ? 0.0f : 1.0f / l_tot;
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
     barrier_no_fence();  // every wave is done with the ring
     const int q0 = qb * BQ + wave * 32;
     const int rows = min(32, a.sq - q0);
     const int qr = lane & 31;
-    if (a.o32) {
+    if (o32) {
         float *st = reinterpret_cast<float *>(smem) + wave * 32 * OP32;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
             }
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
         __builtin_amdgcn_wave_barrier();
-        float *dst = a.o32 + ((int64_t)head * a.sq + q0) * D;
+        float *dst = o32 + ((int64_t)head * a.sq + q0) * D;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = 2 * i + (lane >> 5), chunk = lane & 31;
@@ -479,8 +485,8 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
                     *reinterpret_cast<const u32x4 *>(st + row * OP16 + 8 * chunk);
         }
     }
-    if (a.lse && h == 0 && q < a.sq) {
-        a.lse[(int64_t)head * a.sq + q] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
+    if (lse_out && h == 0 && q < a.sq) {
+        lse_out[(int64_t)head * a.sq + q] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
     }
 }
 
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     if (a.sq <= 0) return hipSuccess;
     const int nqb = (a.sq + BQ - 1) / BQ;
-    const int blocks = nqb * a.num_heads;
+    const int blocks = nqb * a.num_heads * (a.n_split > 1 ? a.n_split : 1);
     hipLaunchKernelGGL(flash_fwd_f16_d128, dim3(blocks), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }

@@ -25,6 +25,10 @@ struct FlashArgs {
     int64_t o16_ld;
     float *o32;
     float *lse;
+    // Key split (0 or 1: none): workgroup item w covers split w / (H * query
+    // blocks), keys [split * split_len, min(skv, (split + 1) * split_len)),
+    // and writes its partial o32 / lse at split * H * sq * d / split * H * sq.
+    int n_split, split_len;
 };
 
 struct FlashArgsF32 {
@@ -100,6 +104,7 @@ struct MergeArgs {
     const float *o_parts;
     const float *lse_parts;
     void *o_out;
+    int64_t o_ld;  // row stride of o_out (elements); 0 means num_heads * head_dim
     int out_f16;
     float *lse_out;
 };

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
         lse = m + logf(total);
     }
     const int64_t ocol = (int64_t)head * a.head_dim + 4 * t;
-    const int64_t ld = (int64_t)a.num_heads * a.head_dim;
+    const int64_t ld = a.o_ld ? a.o_ld : (int64_t)a.num_heads * a.head_dim;
     if (a.out_f16) {
         half4 hv;
 #pragma unroll

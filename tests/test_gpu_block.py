@@ -96,7 +96,8 @@ def test_tiny_config_fp32_rank_share_four_chunks():
     blk.close()
 
 
-@pytest.mark.parametrize("seq,h,nh", [(1000, 512, 4), (300, 384, 3), (1, 256, 2), (7, 128, 1), (520, 1024, 8)])
+@pytest.mark.parametrize("seq,h,nh", [(1000, 512, 4), (300, 384, 3), (1, 256, 2), (7, 128, 1), (520, 1024, 8),
+                                      (2000, 256, 2)])
 def test_block_f16_small_all_rows(seq, h, nh):
     _check_all_rows(seq, h, nh, np.float16, 5e-3, 2e-2)
 

@@ -166,6 +166,24 @@ def test_tp_share_f16_small_all_rows(seq, h, nh, n):
     assert_close(total, oracle.block_forward(x, *ws, nh), what="sum of partials (all-reduce)")
 
 
+@pytest.mark.parametrize("seq,h,nh,n", [(2048, 1024, 8, 4), (1500, 512, 4, 2)])
+def test_tp_share_key_split_all_rows(seq, h, nh, n):
+    # few heads per rank: the attention splits its keys into ranges merged by LSE
+    say(f"TP share with key-split attention S={seq} h={h} H={nh} N={n}")
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=34)
+    hl, d = nh // n, h // nh
+    for r in (0, n - 1):
+        blk = B.AttnBlock(*(dev(w) for w in ws), nh, seq, n_ranks=n, rank=r)
+        attn = torch.empty((seq, hl * d), dtype=torch.float16, device="cuda")
+        lse = torch.empty((hl, seq), dtype=torch.float32, device="cuda")
+        y = blk.forward(dev(x), taps=B.Taps(None, None, None, attn.data_ptr(), lse.data_ptr(), 0))
+        blk.close()
+        assert_close(host(y), shares.tp_share(x, *ws, nh, n, r), what=f"rank {r} partial y")
+        ref = oracle.block_forward(x, *ws, nh, taps=True)
+        assert_close(host(attn), ref["o"][:, r * hl * d:(r + 1) * hl * d], what=f"rank {r} attention output")
+        assert_close(host(lse), ref["lse"][r * hl:(r + 1) * hl], what=f"rank {r} LSE")
+
+
 def test_tp_share_tiny_fp32():
     seq, h, nh, n = 256, 256, 4, 4
     say("TP share tiny fp32, 4 ranks")
