@@ -265,8 +265,6 @@ __device__ __forceinline__ void update_max(float mt, float &m_run, float &l_run,
 __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
                                             floatx16 (&o)[4], const half8 (&qf)[8], half8 (&fr)[RA],
                                             float &m_run, float &l_run) {
-    issue_k_full(c, t + 4, t + 3);
-    issue_v_full(c, t + 3, t + 3);
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
     half8 pf[4];
@@ -276,6 +274,10 @@ __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[
         const half8 a = fr[n % RA];
         const int m = n + RA;
         fr[n % RA] = rd(m < 32 ? cur + m * FRAG : nxt + (m - 32) * FRAG);
+        // stage t+3's direct loads go out a few MFMAs into each half of the
+        // step rather than in one burst at its start
+        if (n == 4) issue_k_full(c, t + 4, t + 3);
+        if (n == 20) issue_v_full(c, t + 3, t + 3);
         if (n < 16) {
             const int kk = n >> 1, kb = n & 1;
             sn[kb] = mfma32(a, qf[kk], kk == 0 ? floatx16{} : sn[kb]);
