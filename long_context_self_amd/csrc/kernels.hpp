@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace attnblk {
 
 // Attention over one key range for every head (fp16 path: head_dim 128;
@@ -95,7 +97,10 @@ struct SegCopyArgs {
     uint32_t n_outer, n_inner;
     int64_t src_so, src_si, dst_so, dst_si;
     uint32_t chunks_per_seg;
-    uint32_t blocks_per_seg;  // set by the launcher
+    // set by the launcher: the 16-byte chunks of all segments form one index
+    // space, split evenly over the workgroups
+    uint32_t total_chunks;
+    FastDiv div_cps, div_inner;
 };
 
 struct MergeArgs {

@@ -8,9 +8,11 @@
 // Every rearrangement here is a batch of equal-length contiguous segments
 // moved between two strided positions, so one kernel serves all of them:
 // segment (o, i) goes from src + o*src_so + i*src_si to dst + o*dst_so +
-// i*dst_si. HBM-bound: 16-byte loads and stores, four per thread in flight;
-// one workgroup covers part of one segment, so the segment index is a
-// per-workgroup scalar.
+// i*dst_si. HBM-bound: the 16-byte chunks of all segments are numbered in
+// one index space that the workgroups split evenly, four chunks per thread in
+// flight, so segments of any length (1 KiB rows as well as 1 MiB blocks) keep
+// every thread busy; a chunk's segment comes from two multiply-shift
+// divisions by launch constants.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -22,34 +24,46 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &d) {
+    return (uint32_t)(((uint64_t)n * d.m) >> (32 + d.s));
+}
+
 __global__ __launch_bounds__(kThreads) void seg_copy(SegCopyArgs a) {
-    const uint32_t seg = blockIdx.x / a.blocks_per_seg;
-    const uint32_t part = blockIdx.x - seg * a.blocks_per_seg;
-    const uint32_t o = seg / a.n_inner;
-    const uint32_t i = seg - o * a.n_inner;
-    const char *s = a.src + o * a.src_so + i * a.src_si;
-    char *d = a.dst + o * a.dst_so + i * a.dst_si;
-    const uint32_t c0 = part * kThreads * kUnroll + threadIdx.x;
+    const uint32_t c0 = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
     u32x4 v[kUnroll];
+    const char *s[kUnroll];
+    char *d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = c0 + u * kThreads;
-        if (c < a.chunks_per_seg) v[u] = ldg16(s + (int64_t)c * 16);
+        const uint32_t id = c0 + u * kThreads;
+        s[u] = nullptr;
+        if (id < a.total_chunks) {
+            const uint32_t seg = fast_div(id, a.div_cps);
+            const uint32_t c = id - seg * a.chunks_per_seg;
+            const uint32_t o = fast_div(seg, a.div_inner);
+            const uint32_t i = seg - o * a.n_inner;
+            s[u] = a.src + o * a.src_so + i * a.src_si + (int64_t)c * 16;
+            d[u] = a.dst + o * a.dst_so + i * a.dst_si + (int64_t)c * 16;
+            v[u] = ldg16(s[u]);
+        }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = c0 + u * kThreads;
-        if (c < a.chunks_per_seg) stg16(d + (int64_t)c * 16, v[u]);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+        if (s[u]) stg16(d[u], v[u]);
 }
 
 }  // namespace
 
 hipError_t launch_seg_copy(SegCopyArgs a, hipStream_t stream) {
     if (a.n_outer == 0 || a.n_inner == 0 || a.chunks_per_seg == 0) return hipSuccess;
-    a.blocks_per_seg = (a.chunks_per_seg + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-    const uint64_t blocks = (uint64_t)a.n_outer * a.n_inner * a.blocks_per_seg;
-    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    const uint64_t total = (uint64_t)a.n_outer * a.n_inner * a.chunks_per_seg;
+    // chunk indices, segment indices and divisors must stay below 2^31
+    if (total >= 0x80000000ull || a.chunks_per_seg >= 0x80000000u || a.n_inner >= 0x80000000u)
+        return hipErrorInvalidConfiguration;
+    a.total_chunks = (uint32_t)total;
+    a.div_cps = make_fast_div(a.chunks_per_seg);
+    a.div_inner = make_fast_div(a.n_inner);
+    const uint64_t blocks = (total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
     hipLaunchKernelGGL(seg_copy, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -9,9 +9,9 @@
 // for Parallel Layer Execution", section 3).
 //
 // HBM-bound: each thread owns four consecutive head dimensions of one
-// (head, query) row, so every part is read in 16-byte coalesced chunks and
-// each part's LSE is read once per row from cache. Parts are summed in index
-// order, so the result is deterministic.
+// (head, query) row, so every part is read in 16-byte coalesced chunks (four
+// parts in flight per thread) and each part's LSE is read once per row from
+// cache. Parts are summed in index order, so the result is deterministic.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -19,6 +19,8 @@
 namespace attnblk {
 
 namespace {
+
+constexpr int kBatch = 4;  // parts whose loads are in flight together
 
 __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
     const int tpr = a.head_dim / 4;  // threads per row
@@ -39,13 +41,29 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
     if (m == -INFINITY) {
         lse = -INFINITY;
     } else {
+        // Parts go kBatch at a time: their loads are all issued before the
+        // first is used, so each thread keeps kBatch 16-byte reads in flight.
+        // The sums still run in part order.
         float total = 0.0f;
-        for (int b = 0; b < a.n_parts; ++b) {
-            const float w = expf(a.lse_parts[b * nrows + row] - m);
-            total += w;
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(a.o_parts + b * part_stride_o +
-                                                                  row * a.head_dim + 4 * t);
-            acc += w * v;
+        for (int b0 = 0; b0 < a.n_parts; b0 += kBatch) {
+            float l[kBatch];
+            floatx4 v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < a.n_parts) {
+                    l[j] = a.lse_parts[(b0 + j) * nrows + row];
+                    v[j] = *reinterpret_cast<const floatx4 *>(a.o_parts + (b0 + j) * part_stride_o + row * a.head_dim +
+                                                             4 * t);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < a.n_parts) {
+                    const float w = expf(l[j] - m);
+                    total += w;
+                    acc += w * v[j];
+                }
+            }
         }
         acc *= 1.0f / total;
         lse = m + logf(total);

@@ -5,6 +5,7 @@
 
 #include <cmath>
 
+#include "fastdiv.hpp"
 #include "validate.hpp"
 
 using namespace attnblk;
@@ -18,7 +19,30 @@ static int failures = 0;
         }                                                             \
     } while (0)
 
+// n / d through make_fast_div's multiplier and shift, as the layout kernel computes it.
+static uint32_t fdiv(uint32_t n, const FastDiv &f) { return (uint32_t)(((uint64_t)n * f.m) >> (32 + f.s)); }
+
 int main() {
+    // fast division: exact for every numerator below 2^31 the layout kernel can produce
+    {
+        const uint32_t ds[] = {1u, 2u, 3u, 5u, 7u, 64u, 512u, 1000u, 4096u, 65535u, 65537u, (1u << 20) + 3u,
+                               (1u << 30) + 1u, 0x7fffffffu};
+        uint64_t x = 88172645463325252ull;  // xorshift64 numerators
+        for (uint32_t d : ds) {
+            const FastDiv f = make_fast_div(d);
+            EXPECT(f.m < (1ull << 33));
+            const uint32_t edge[] = {0u, 1u, d - 1u, d, d + 1u, 2u * d - 1u, 0x7fffffffu};
+            for (uint32_t n : edge)
+                if (n < 0x80000000u) EXPECT(fdiv(n, f) == n / d);
+            for (int i = 0; i < 20000; ++i) {
+                x ^= x << 13;
+                x ^= x >> 7;
+                x ^= x << 17;
+                const uint32_t n = (uint32_t)(x & 0x7fffffffu);
+                EXPECT(fdiv(n, f) == n / d);
+            }
+        }
+    }
     const void *P = reinterpret_cast<const void *>(0x1000);
     const float *F = reinterpret_cast<const float *>(0x1000);
     // create
