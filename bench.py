@@ -15,7 +15,8 @@ region, on the stream the kernels run on.
 The same run also times, in the same way, the other workloads: seq 16384 /
 32768 / 65536 at hidden 4096, seq 8192 at hidden 8192 (64 heads), the
 context-parallel rank share (a 4096-row query chunk of seq 32768 against K/V in
-8 blocks of 4096, partials + LSE merge) and 6 stacked blocks at seq 32768.
+8 blocks of 4096, partials + LSE merge, beside the same chunk against all keys in
+one launch) and 6 stacked blocks at seq 32768.
 The CPU baseline is the fp64 oracle, timed on a bounded sample of the headline
 workload on this host's cores.
 
@@ -175,30 +176,45 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
     stream = torch.cuda.current_stream().cuda_stream
     evs = hip.events(3 * steps)
 
-    def one(s):
-        if s is not None:
-            hip.record(evs[3 * s], stream)
+    def timed(partials):
+        """Median ms of `partials()` and of the merge that follows it."""
+        def one(s):
+            if s is not None:
+                hip.record(evs[3 * s], stream)
+            partials()
+            if s is not None:
+                hip.record(evs[3 * s + 1], stream)
+            B.attn_merge_lse(ranks, nh, d, chunk, o_parts, lse_parts, o, torch.float16)
+            if s is not None:
+                hip.record(evs[3 * s + 2], stream)
+
+        for _ in range(warmup):
+            one(None)
+        torch.cuda.synchronize()
+        for s in range(steps):
+            one(s)
+        torch.cuda.synchronize()
+        return (stats([hip.ms(evs[3 * s], evs[3 * s + 1]) for s in range(steps)]),
+                stats([hip.ms(evs[3 * s + 1], evs[3 * s + 2]) for s in range(steps)]))
+
+    # the 8 block partials, one attn_partial_forward launch per block
+    def per_block():
         for b in range(ranks):
             B.attn_partial_forward(nh, d, q, chunk, seq * d, k[:, b * chunk:], chunk, seq * d,
                                    vt[:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b])
-        if s is not None:
-            hip.record(evs[3 * s + 1], stream)
-        B.attn_merge_lse(ranks, nh, d, chunk, o_parts, lse_parts, o, torch.float16)
-        if s is not None:
-            hip.record(evs[3 * s + 2], stream)
-
-    for _ in range(warmup):
-        one(None)
+    ps, ms_ = timed(per_block)
+    # comparison: the same chunk against all 32768 keys in one launch (no blocks, no merge)
+    for s in range(warmup + steps):
+        if s >= warmup:
+            hip.record(evs[3 * (s - warmup)], stream)
+        B.attn_partial_forward(nh, d, q, chunk, seq * d, k, seq, seq * d, vt, d * ld, ld, o_parts[0], lse_parts[0])
+        if s >= warmup:
+            hip.record(evs[3 * (s - warmup) + 1], stream)
     torch.cuda.synchronize()
-    for s in range(steps):
-        one(s)
-    torch.cuda.synchronize()
-    part = [hip.ms(evs[3 * s], evs[3 * s + 1]) for s in range(steps)]
-    merge = [hip.ms(evs[3 * s + 1], evs[3 * s + 2]) for s in range(steps)]
+    one_shot = stats([hip.ms(evs[3 * s], evs[3 * s + 1]) for s in range(steps)])
     hip.destroy(evs)
     flops = 4.0 * chunk * seq * h
     merge_bytes = ranks * chunk * h * 4 + ranks * nh * chunk * 4 + chunk * h * 2
-    ps, ms_ = stats(part), stats(merge)
     del q, k, vt, o_parts, lse_parts, o
     torch.cuda.empty_cache()
     return {
@@ -209,6 +225,8 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
         "merge_gbs": merge_bytes / (ms_["median"] * 1e-3) / 1e9,
         "merge_frac_of_hbm": merge_bytes / (ms_["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "merge_bytes": merge_bytes,
+        "one_shot_ms": one_shot["median"],
+        "one_shot_attention_tflops": flops / (one_shot["median"] * 1e-3) / 1e12,
     }
 
 
@@ -565,7 +583,7 @@ def main() -> int:
         log("rank share")
         extra.append(run_rank_share(torch, B, hip, w, st))
         log(f"  {extra[-1]['ms']:.3f} ms, attention {extra[-1]['attention_tflops']:.0f} TFLOP/s, merge "
-            f"{extra[-1]['merge_gbs']:.0f} GB/s")
+            f"{extra[-1]['merge_gbs']:.0f} GB/s; one launch over all keys {extra[-1]['one_shot_ms']:.3f} ms")
         log("Ulysses share (rank 0 of 8), seq 32768")
         extra.append(run_ulysses_share(torch, B, hip, w, st))
         log(f"  {extra[-1]['ms']:.3f} ms: gather {extra[-1]['gather_gbs']:.0f} GB/s, attention "
