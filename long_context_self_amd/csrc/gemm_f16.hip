@@ -10,13 +10,18 @@
 // "What is hint.json?".
 //
 // Design (MI355X): 256x256 tile per workgroup, 8 waves (2 per SIMD) of
-// 128x64 each on v_mfma_f32_32x32x16_f16. K advances in steps of 32 through a
-// four-stage LDS ring filled by direct global->LDS loads (no staging
-// registers), issued three steps ahead; one barrier per step. An XOR swizzle
-// applied on the load side makes every ds_read_b128 conflict-free. Tiles are grouped 4 deep
-// in M and each XCD gets a contiguous range of tiles so its L2 holds the A
-// and B panels its workgroups share. The epilogue stages the fp16 tile in
-// LDS (transposed for V) and writes 16-byte chunks.
+// 128x64 each on v_mfma_f32_16x16x32_f16, whose 4-register accumulators move
+// fewer register-file bytes per flop than the 32x32 form and so leave the
+// chip more clock under its power limit. K advances in steps of 64 through two
+// LDS buffers: each thread loads its share of step k+2 into registers while
+// step k is computed and stores step k+1 (loaded one step earlier) into the
+// other buffer; one barrier per step. Scheduling groups pin the steady step's
+// order: the first k-substep's 32 MFMAs are each paired with one LDS store,
+// global load or next-substep fragment read. An XOR swizzle makes every LDS
+// read and write conflict-free. Tiles are grouped 4 deep in M and each XCD
+// gets a contiguous range of tiles so its L2 holds the A and B panels its
+// workgroups share. The epilogue stages the fp16 tile in LDS (transposed for
+// V) and writes 16-byte chunks.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -25,52 +30,49 @@ namespace attnblk {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int NTHREADS = 512;
-constexpr int STAGES = 4;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NTHREADS = 512;   // 8 waves (two per SIMD), 2 x 4 of 128 x 64
 constexpr int GROUP_M = 4;
 constexpr int A_TILE = BM * BK;  // halves
 constexpr int B_TILE = BN * BK;
-constexpr int STAGE = A_TILE + B_TILE;
+constexpr int BUF = A_TILE + B_TILE;
+constexpr int NBUF = 2;
 constexpr int CP = BN + 8;       // epilogue pitch (halves)
-constexpr int SMEM_MAIN = STAGES * STAGE * 2;  // bytes
+constexpr int SMEM_MAIN = NBUF * BUF * 2;  // bytes
 constexpr int SMEM_EPI = BM * CP * 2;
 constexpr int SMEM_BYTES = SMEM_MAIN > SMEM_EPI ? SMEM_MAIN : SMEM_EPI;
+constexpr int LPT = (BM * BK / 8) / NTHREADS;  // 16-byte chunks per thread per operand tile (4)
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
+// LDS tile layout: 128-byte rows of eight 16-byte chunks; logical chunk c of
+// row r sits at physical chunk c ^ swz(r). Sixteen consecutive rows then
+// cover every (row parity, chunk) pair once, so a ds_read_b128 of one chunk
+// column over 16 rows, and a ds_write_b128 of 2 rows x 8 chunks, hit distinct
+// banks. swz uses bits 1-3 of the row only, which are the same for rows 32
+// apart, so every fragment address is a per-lane base plus an immediate.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// LDS tile layout: 64-byte rows of four 16-byte chunks; logical chunk c of
-// row r sits at physical chunk c ^ swz(r), which spreads the 16 rows one LDS
-// pass reads over all 16 bank groups. swz depends only on bits 2-3 of the
-// row, which are the same for the four row blocks (32 rows apart) a wave
-// reads, so a fragment address is one base register plus an immediate.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
-
-
-// Issue the direct global->LDS loads of one K-step (A rows and B rows) into
-// stage buffer `st`. A global_load_lds_dwordx4 writes 64 lanes x 16 bytes to
-// consecutive LDS addresses, so each lane fetches the global chunk that its
-// LDS slot must hold. Waves 0-3 move A (16 instructions), waves 4-7 move B.
-// Interior tiles use one loop-invariant lane offset; edge tiles clamp rows
-// past M or N to the last valid row.
-template <bool EDGE>
-__device__ __forceinline__ void issue_stage(const GemmArgs &g, half_t *st, int m0, int n0, int k0, int wave,
-                                            int lane) {
-    const bool is_a = wave < 4;
-    const int w4 = wave & 3;
-    const half_t *base = is_a ? g.a : g.b;
-    const int64_t ld = is_a ? g.lda : g.ldb;
-    const int r0 = is_a ? m0 : n0;
-    const int rmax = (is_a ? g.M : g.N) - 1;
-    half_t *tile = st + (is_a ? 0 : A_TILE);
-    const int lrow = lane >> 2;                  // row within a 16-row instruction block
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk for this LDS slot
+// Global -> registers: thread t holds chunk t % 8 of rows t / 8 + 64 j,
+// j = 0..3, of the A tile and of the B tile for k-step k0. Rows past M or N
+// are clamped to the last row (their results are never stored).
+__device__ __forceinline__ void load_tile(const GemmArgs &g, int m0, int n0, int k0, int tid, u32x4 (&ra)[LPT],
+                                          u32x4 (&rb)[LPT]) {
+    const int r = tid >> 3, c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int n = 4 * w4 + i;                // instruction index 0..15: rows 16n..16n+15
-        int row = r0 + 16 * n + lrow;
-        if (EDGE) row = min(row, rmax);
-        const half_t *src = base + (int64_t)row * ld + k0 + chunk * 8;
-        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(tile + n * 512), 16, 0, 0);
+    for (int j = 0; j < LPT; ++j) {
+        const int ma = min(m0 + r + 64 * j, g.M - 1), nb = min(n0 + r + 64 * j, g.N - 1);
+        ra[j] = ldg16(g.a + (int64_t)ma * g.lda + k0 + 8 * c);
+        rb[j] = ldg16(g.b + (int64_t)nb * g.ldb + k0 + 8 * c);
+    }
+}
+
+// Registers -> LDS buffer (swizzled). wo is this thread's offset in halves.
+__device__ __forceinline__ void store_tile(half_t *buf, int wo, const u32x4 (&ra)[LPT], const u32x4 (&rb)[LPT]) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        *reinterpret_cast<u32x4 *>(buf + wo + j * 64 * BK) = ra[j];
+        *reinterpret_cast<u32x4 *>(buf + A_TILE + wo + j * 64 * BK) = rb[j];
     }
 }
 
@@ -81,7 +83,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5;
     const int wm = wave >> 2;  // 0..1 -> rows wm*128
     const int wn = wave & 3;   // 0..3 -> cols wn*64
 
@@ -98,117 +99,120 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     const int m0 = tm * BM, n0 = tn * BN;
     // published to every wave by the barriers of the main loop
     if (g.row_scale && tid < BM) rs_tile[tid] = g.row_scale[min(m0 + tid, g.M - 1)];
-    const bool edge = (m0 + BM > g.M) || (n0 + BN > g.N);
 
-    floatx16 acc[4][2];
+    floatx4 acc[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{};
 
     const int nk = g.K / BK;
-    // prologue: stages 0..STAGES-2 in flight
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) {
-            if (edge)
-                issue_stage<true>(g, smem + s * STAGE, m0, n0, s * BK, wave, lane);
-            else
-                issue_stage<false>(g, smem + s * STAGE, m0, n0, s * BK, wave, lane);
-        }
-
-    // fragment bases: row (lane & 31) of each 32-row block, physical chunk for k-substep kk
-    const int sw = swz(lane & 31);
-    const int a_off0 = (wm * 128 + (lane & 31)) * BK + (((0 + h) ^ sw) << 3);
-    const int a_off1 = (wm * 128 + (lane & 31)) * BK + (((2 + h) ^ sw) << 3);
-    const int b_off0 = A_TILE + (wn * 64 + (lane & 31)) * BK + (((0 + h) ^ sw) << 3);
-    const int b_off1 = A_TILE + (wn * 64 + (lane & 31)) * BK + (((2 + h) ^ sw) << 3);
-
-    // Software pipeline over K substeps of 16: the fragment reads of substep
-    // t+1 are issued before the MFMAs of substep t. Barrier B_kt sits between
-    // the two substeps of step kt: every wave has then finished reading step
-    // kt-1 (its fragments fed MFMAs before B_kt), so its buffer can be refilled
-    // with step kt+STAGES-1; and each wave waited for its own loads of step
-    // kt+1 before B_kt, so step kt+1 is readable after it.
-    auto read_frags = [&](const half_t *stb, int kk, half8 (&af)[4], half8 (&bf)[2]) {
-        const half_t *ab = stb + (kk ? a_off1 : a_off0);
-        const half_t *bb = stb + (kk ? b_off1 : b_off0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const half8 *>(ab + i * 32 * BK);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const half8 *>(bb + j * 32 * BK);
-    };
-    auto mma = [&](const half8 (&af)[4], const half8 (&bf)[2]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
-    };
-    // stage 0 readable (stages 1 and 2, 4 loads each, may stay in flight)
-    static_assert(STAGES == 4, "the waits below count 4 loads per stage and 3 stages in flight");
-    if (nk >= 3)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
-    else if (nk == 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(4));
-    else
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    const int wo = (tid >> 3) * BK + (((tid & 7) ^ swz(tid >> 3)) << 3);
+    u32x4 ra[LPT], rb[LPT];
+    // prologue: k-step 0 into buffer 0, k-step 1 into registers
+    load_tile(g, m0, n0, 0, tid, ra, rb);
+    store_tile(smem, wo, ra, rb);
+    if (nk > 1) load_tile(g, m0, n0, BK, tid, ra, rb);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));  // this wave's LDS stores are done
     barrier_no_fence();
-    half8 a0[4], b0[2], a1[4], b1[2];
-    read_frags(smem, 0, a0, b0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const half_t *stb = smem + (kt % STAGES) * STAGE;
-        read_frags(stb, 1, a1, b1);
-        mma(a0, b0);
-        if (kt + 1 < nk) {
-            // step kt+1 must be complete; steps up to kt+STAGES-2 may stay in flight
-            const int in_flight = min(nk - 1, kt + STAGES - 2) - (kt + 1);
-            if (in_flight >= 1)
-                __builtin_amdgcn_s_waitcnt(vmcnt_only(4));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-            barrier_no_fence();
-            if (kt + STAGES - 1 < nk) {
-                const int sidx = (kt + STAGES - 1) % STAGES;
-                if (edge)
-                    issue_stage<true>(g, smem + sidx * STAGE, m0, n0, (kt + STAGES - 1) * BK, wave, lane);
-                else
-                    issue_stage<false>(g, smem + sidx * STAGE, m0, n0, (kt + STAGES - 1) * BK, wave, lane);
-            }
-            read_frags(smem + ((kt + 1) % STAGES) * STAGE, 0, a0, b0);
-        }
-        mma(a1, b1);
+
+    // fragment bases (16x16x32 layout): row (lane & 15) of each 16-row block;
+    // physical chunk of k-substep kk (logical chunk 4 kk + lane / 16)
+    const int sw = swz(lane & 15);
+    const int q4 = lane >> 4;
+    int a_off[2], b_off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        a_off[kk] = (wm * 128 + (lane & 15)) * BK + (((4 * kk + q4) ^ sw) << 3);
+        b_off[kk] = A_TILE + (wn * 64 + (lane & 15)) * BK + (((4 * kk + q4) ^ sw) << 3);
     }
-    __syncthreads();  // every wave is done with the stage buffers; reuse LDS for the epilogue
+    auto read_frags = [&](const half_t *buf, int kk, half8 (&af)[8], half8 (&bf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const half8 *>(buf + a_off[kk] + i * 16 * BK);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const half8 *>(buf + b_off[kk] + j * 16 * BK);
+    };
+    auto mma = [&](const half8 (&af)[8], const half8 (&bf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Step kt computes from buffer kt % 2. After its first k-substep it stores
+    // k-step kt+1 (in registers) into the other buffer -- last read in step
+    // kt-1, before the barrier that ended it -- and loads k-step kt+2 into the
+    // registers. The barrier at the end of step kt publishes k-step kt+1.
+    half8 a0[8], b0[4], a1[8], b1[4];
+    auto step = [&](int kt, bool store, bool load) {
+        const half_t *buf = smem + (kt & 1) * BUF;
+        half_t *nbuf = smem + ((kt + 1) & 1) * BUF;
+        read_frags(buf, 0, a0, b0);
+        mma(a0, b0);
+        if (store) store_tile(nbuf, wo, ra, rb);
+        if (load) load_tile(g, m0, n0, (kt + 2) * BK, tid, ra, rb);
+        read_frags(buf, 1, a1, b1);
+        mma(a1, b1);
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {  // steady steps: store and load
+        step(kt, true, true);
+        // Issue order: the 12 fragment reads of k-substep 0; then its MFMAs,
+        // each followed by one of: the 8 LDS stores of step kt+1, the 8
+        // global loads of step kt+2, the 12 fragment reads of k-substep 1;
+        // then the remaining MFMAs.
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 12, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 36, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));  // LDS stores and reads of this wave done
+        barrier_no_fence();
+    }
+    for (; kt < nk; ++kt) {  // the last two steps
+        step(kt, kt + 1 < nk, false);
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+        barrier_no_fence();
+    }
 
     // ---- epilogue: stage the fp16 tile in LDS, then 16-byte stores
     const bool v_tile = g.mode == kQkv && n0 >= 2 * g.hidden;
     // A tile may straddle the Q|K border at column h (odd head counts), so the
     // pre-scale is chosen per column; the V border 2h is a multiple of 256.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            const int col = wn * 64 + j * 16 + (lane & 15);
             const float sc = (g.mode == kQkv && n0 + col < g.hidden) ? g.q_scale : 1.0f;
+            const int row = wm * 128 + i * 16 + 4 * q4;
+            // RMSNorm pre-norm: output row m scales by 1 / rms(x_m)
+            float rsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (g.row_scale) {
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int row = wm * 128 + i * 32 + 8 * gg + 4 * h;
-                // RMSNorm pre-norm: output row m scales by 1 / rms(x_m)
-                float rsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-                if (g.row_scale) {
+                for (int r = 0; r < 4; ++r) rsc[r] = rs_tile[row + r];
+            }
+            if (v_tile) {
+                half4 v;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) rsc[r] = rs_tile[row + r];
-                }
-                if (v_tile) {
-                    half4 v;
+                for (int r = 0; r < 4; ++r) v[r] = (half_t)(acc[i][j][r] * rsc[r]);
+                *reinterpret_cast<half4 *>(smem + col * CP + row) = v;
+            } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = (half_t)(acc[i][j][4 * gg + r] * rsc[r]);
-                    *reinterpret_cast<half4 *>(smem + col * CP + row) = v;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        smem[(row + r) * CP + col] = (half_t)(acc[i][j][4 * gg + r] * rsc[r] * sc);
-                }
+                for (int r = 0; r < 4; ++r) smem[(row + r) * CP + col] = (half_t)(acc[i][j][r] * rsc[r] * sc);
             }
         }
     __syncthreads();
@@ -262,6 +266,7 @@ __global__ __launch_bounds__(256) void transpose_f16(const half_t *src, int rows
 
 hipError_t launch_gemm_f16(const GemmArgs &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (g.K <= 0 || g.K % BK != 0) return hipErrorInvalidValue;  // K = h or H d, a multiple of 64
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     hipLaunchKernelGGL(gemm_f16_nt, dim3(tiles), dim3(NTHREADS), 0, stream, g);
     return hipGetLastError();
