@@ -16,8 +16,8 @@
 // LDS buffers: each thread loads its share of step k+2 into registers while
 // step k is computed and stores step k+1 (loaded one step earlier) into the
 // other buffer; one barrier per step. Scheduling groups pin the steady step's
-// order: the first k-substep's 32 MFMAs are each paired with one LDS store,
-// global load or next-substep fragment read. An XOR swizzle makes every LDS
+// order, spreading the LDS stores, the next substep's fragment reads and the
+// global loads among the MFMAs. An XOR swizzle makes every LDS
 // read and write conflict-free. Tiles are grouped 4 deep in M and each XCD
 // gets a contiguous range of tiles so its L2 holds the A and B panels its
 // workgroups share. The epilogue stages the fp16 tile in LDS (transposed for
@@ -158,27 +158,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
     int kt = 0;
     for (; kt + 2 < nk; ++kt) {  // steady steps: store and load
         step(kt, true, true);
-        // Issue order: the 12 fragment reads of k-substep 0; then its MFMAs,
-        // each followed by one of: the 8 LDS stores of step kt+1, the 8
-        // global loads of step kt+2, the 12 fragment reads of k-substep 1;
-        // then the remaining MFMAs.
+        // Issue order: the 12 fragment reads of k-substep 0; its MFMAs in
+        // pairs, each pair followed by one of the 8 LDS stores of step kt+1;
+        // one MFMA per fragment read of k-substep 1; then MFMAs in pairs, each
+        // pair followed by one of the 8 global loads of step kt+2; the rest.
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 12, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
             __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
         }
 #pragma unroll
         for (int i = 0; i < 12; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 36, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 20, 0);
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));  // LDS stores and reads of this wave done
         barrier_no_fence();
     }
