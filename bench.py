@@ -15,8 +15,9 @@ region, on the stream the kernels run on.
 The same run also times, in the same way, the other workloads: seq 16384 /
 32768 / 65536 at hidden 4096, seq 8192 at hidden 8192 (64 heads), the
 context-parallel rank share (a 4096-row query chunk of seq 32768 against K/V in
-8 blocks of 4096, partials + LSE merge, beside the same chunk against all keys in
-one launch) and 6 stacked blocks at seq 32768.
+8 blocks of 4096: the block partials alternate over two streams, then the LSE
+merge; beside it the same chunk against all keys in one launch) and 6 stacked
+blocks at seq 32768.
 The CPU baseline is the fp64 oracle, timed on a bounded sample of the headline
 workload on this host's cores.
 
@@ -197,11 +198,24 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
         return (stats([hip.ms(evs[3 * s], evs[3 * s + 1]) for s in range(steps)]),
                 stats([hip.ms(evs[3 * s + 1], evs[3 * s + 2]) for s in range(steps)]))
 
-    # the 8 block partials, one attn_partial_forward launch per block
+    # the 8 block partials, one attn_partial_forward launch per block. They are
+    # independent (each writes its own part), so they alternate over the
+    # caller's stream and a second one; the tail of one launch then overlaps
+    # the start of the next. The merge waits for both.
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
     def per_block():
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
         for b in range(ranks):
+            st = main if b % 2 == 0 else side
             B.attn_partial_forward(nh, d, q, chunk, seq * d, k[:, b * chunk:], chunk, seq * d,
-                                   vt[:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b])
+                                   vt[:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b], stream=st.cuda_stream)
+        join = torch.cuda.Event()
+        join.record(side)
+        main.wait_event(join)
     ps, ms_ = timed(per_block)
     # comparison: the same chunk against all 32768 keys in one launch (no blocks, no merge)
     for s in range(warmup + steps):
@@ -218,7 +232,8 @@ def run_rank_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
     del q, k, vt, o_parts, lse_parts, o
     torch.cuda.empty_cache()
     return {
-        "workload": "rank share: 4096-row query chunk of seq 32768 vs K/V in 8 blocks of 4096, hidden 4096, 32 heads",
+        "workload": "rank share: 4096-row query chunk of seq 32768 vs K/V in 8 blocks of 4096, hidden 4096, 32 heads "
+                    "(block partials alternating over two streams)",
         "ms": ps["median"] + ms_["median"], "partials_ms": ps, "merge_ms": ms_,
         "attention_tflops": flops / (ps["median"] * 1e-3) / 1e12,
         "attention_frac_of_peak": flops / (ps["median"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
