@@ -189,6 +189,44 @@ def test_two_runs_are_bit_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_partials_on_two_streams_match_one_stream():
+    """attn_partial_forward keeps no state between calls, so block partials
+    enqueued alternately on two streams (each into its own output) equal the
+    same calls on one stream bit for bit, and so does their merge."""
+    say("block partials on two streams")
+    h, sq, skv, d, n = 4, 512, 4096, 128, 4
+    q, k, v = attention_inputs(h, sq, skv, d, seed=12)
+    qd, kd = dev(q), dev(k)
+    vt = dev(to_vt(v))
+    ld, blk = vt.shape[2], skv // n
+
+    def run(streams):
+        o = torch.empty((n, h, sq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((n, h, sq), dtype=torch.float32, device="cuda")
+        main = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        for st in streams:
+            st.wait_event(fork)
+        for b in range(n):
+            st = streams[b % len(streams)]
+            B.attn_partial_forward(h, d, qd, sq, qd.stride(0), kd[:, b * blk:], blk, kd.stride(0), vt[:, :, b * blk:],
+                                   vt.stride(0), ld, o[b], lse[b], stream=st.cuda_stream)
+        for st in streams:
+            join = torch.cuda.Event()
+            join.record(st)
+            main.wait_event(join)
+        out = torch.empty((sq, h * d), dtype=torch.float16, device="cuda")
+        B.attn_merge_lse(n, h, d, sq, o, lse, out, torch.float16)
+        torch.cuda.synchronize()
+        return o, lse, out
+
+    one = run([torch.cuda.current_stream()])
+    two = run([torch.cuda.current_stream(), torch.cuda.Stream()])
+    for a, b2 in zip(one, two):
+        assert torch.equal(a, b2)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_partial_f32_vs_oracle(d):
     say(f"partial f32 d={d}")
