@@ -22,6 +22,13 @@ pin. What each pin rests on:
 * RMSNorm        -- brute force; torch.nn.functional.rms_norm in float64 (and a
                     torch pre-norm + MultiheadAttention block); closed forms of
                     constant rows; invariants (unit mean square, scale and sign).
+* stacking       -- the multi-layer model ("TensorRT Multi-Device (multi-GPU)
+                    support", "Validation (TRT 11.0)", multi-layer model) as
+                    plain composition: the brute-force block, and torch's
+                    MultiheadAttention, applied layer after layer, each layer
+                    fed the previous layer's output (with and without
+                    pre-norm); weights sharp enough that the layers' order and
+                    their chaining both change the result.
 """
 
 from __future__ import annotations
@@ -343,9 +350,67 @@ def pin_rmsnorm_invariants(orc, tol=1e-12):
     return not bad, f"RMSNorm invariant errors {errs}"
 
 
+# ------------------------------------------------------------------- stacking
+def _stack_case(rng, s, h, n_layers, use_norm):
+    """Input and n_layers independent weight sets. W_Q and W_K with std
+    3/sqrt(h) keep every layer's softmax sharp, so the rows stay distinct
+    (relative row spread above 0.18 after every layer of these cases) instead
+    of collapsing to one vector, and the layers do not commute; W_V and W_O
+    have std 1.5/sqrt(h)."""
+    x = rng.standard_normal((s, h)) * 1.5
+    layers = [tuple(rng.standard_normal((h, h)) * (f / math.sqrt(h)) for f in (3.0, 3.0, 1.5, 1.5))
+              for _ in range(n_layers)]
+    norms = None
+    if use_norm:
+        norms = [(rng.uniform(0.5, 1.5, size=h), [1e-6, 1e-3, 0.05][i % 3]) for i in range(n_layers)]
+    return x, layers, norms
+
+
+def pin_stack_bruteforce(orc, tol=1e-12):
+    """stack_forward against the brute-force block applied layer by layer,
+    layer l fed layer l-1's output (1 layer: the block itself)."""
+    worst = 0.0
+    cases = [(5, 4, 1, 1, False), (6, 8, 2, 2, False), (7, 6, 3, 3, False), (6, 8, 2, 3, True),
+             (5, 4, 2, 2, True)]
+    for seed, (s, h, nh, n_layers, use_norm) in enumerate(cases):
+        rng = _rng(800 + seed)
+        x, layers, norms = _stack_case(rng, s, h, n_layers, use_norm)
+        cur = x
+        for i, (wq, wk, wv, wo) in enumerate(layers):
+            if norms is not None:
+                cur = brute.rms_norm(cur, norms[i][0], norms[i][1])
+            cur, _, _ = brute.block(cur, wq, wk, wv, wo, nh)
+        worst = max(worst, _rel(orc.stack_forward(x, layers, nh, norms=norms), cur))
+    return worst <= tol, f"max rel err vs brute-force layer-by-layer stack {worst:.3e}"
+
+
+def pin_stack_torch(orc, tol=1e-10):
+    """stack_forward against torch.nn.MultiheadAttention (bias off, float64)
+    applied layer after layer, with and without torch's rms_norm before each
+    layer."""
+    import torch
+    import torch.nn.functional as F
+
+    worst = 0.0
+    for seed, (s, h, nh, n_layers, use_norm) in enumerate([(40, 64, 4, 3, False), (33, 48, 3, 4, True)]):
+        rng = _rng(850 + seed)
+        x, layers, norms = _stack_case(rng, s, h, n_layers, use_norm)
+        cur = torch.from_numpy(x)[None]
+        with torch.no_grad():
+            for i, (wq, wk, wv, wo) in enumerate(layers):
+                mha = torch.nn.MultiheadAttention(h, nh, bias=False, batch_first=True, dtype=torch.float64)
+                mha.in_proj_weight.copy_(torch.from_numpy(np.concatenate([wq.T, wk.T, wv.T], 0)))
+                mha.out_proj.weight.copy_(torch.from_numpy(wo.T.copy()))
+                if norms is not None:
+                    cur = F.rms_norm(cur, (h,), weight=torch.from_numpy(norms[i][0]), eps=norms[i][1])
+                cur, _ = mha(cur, cur, cur, need_weights=False)
+        worst = max(worst, _rel(orc.stack_forward(x, layers, nh, norms=norms), cur[0].numpy()))
+    return worst <= tol, f"max rel err vs torch MultiheadAttention layer by layer {worst:.3e}"
+
+
 ALL_PINS = [
     pin_bruteforce, pin_bruteforce_attention, pin_closed_forms, pin_torch_mha,
     pin_torch_sdpa, pin_invariants, pin_symmetries, pin_merge, pin_merge_rows,
     pin_linearity, pin_rmsnorm_bruteforce, pin_rmsnorm_torch, pin_rmsnorm_closed_forms,
-    pin_rmsnorm_invariants,
+    pin_rmsnorm_invariants, pin_stack_bruteforce, pin_stack_torch,
 ]

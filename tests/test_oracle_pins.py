@@ -52,6 +52,10 @@ MUTANTS = [
     ("rms_norm_skipped", [("x = rms_norm(x, norm[0], norm[1])", "x = x")]),
     ("rms_norm_after_projection", [("x = rms_norm(x, norm[0], norm[1])", "x = x * 1.0"),
                                    ("y = project(o, wo)", "y = project(o, wo) if norm is None else rms_norm(project(o, wo), norm[0], norm[1])")]),
+    ("stack_unchained", [("y = block_forward(y, wq, wk, wv, wo, num_heads,", "y = block_forward(as_f64(x), wq, wk, wv, wo, num_heads,")]),
+    ("stack_reversed", [("in enumerate(layers):", "in enumerate(layers[::-1]):")]),
+    ("stack_drops_last_layer", [("in enumerate(layers):", "in enumerate(layers[:-1]):")]),
+    ("stack_first_norm_only", [("else norms[i])", "else norms[0])")]),
 ]
 
 
