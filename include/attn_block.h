@@ -54,7 +54,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_E_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment */
     ATTN_E_UNSUPPORTED = 2, /* valid but not implemented (head_dim, batch, dtype) */
-    ATTN_E_OOM = 3,         /* device allocation failed (create only) */
+    ATTN_E_OOM = 3,         /* device allocation failed (create calls, attn_partial_forward's staging) */
     ATTN_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } attn_status_t;
 
@@ -88,6 +88,13 @@ typedef struct attn_block attn_block_t;
  *             before the QKV projection, after it, after attention and after
  *             the output projection (kernel timing in the real launch
  *             configuration). With qkv_only only the first two are recorded.
+ *   v         [H][S][d]   V = X W_V head-major, row-major like q_scaled and k
+ *             (the layout attn_partial_forward takes). Written by a transpose
+ *             of the V^T the projection produces, so it costs one extra pass
+ *             over V (read + write of S*h elements) when requested.
+ * [Taps of the projection's outputs: "Multi-Device Attention Inference with
+ * TensorRT", "What is hint.json?" (the q_scaled tensor feeds QK^T; Q stays
+ * local while K/V are gathered, so a rank's inputs are these tensors).]
  */
 typedef struct {
     void *q_scaled;
@@ -97,11 +104,17 @@ typedef struct {
     float *lse;
     int qkv_only;
     hipEvent_t *events;
+    void *v;
 } attn_taps_t;
 
 /*
  * attn_block_create -- pack the four projection weights into library-owned
  * device memory and allocate the workspace for up to max_tokens rows.
+ * [The block's weights W_Q, W_K, W_V, W_O applied as Y = X W: "Tensor
+ * Parallelism: Sharding Weights for Parallel Layer Execution", section 1 and
+ * section 3, steps 1 and 4; hidden 4096 = 32 heads of 128 in fp16:
+ * "Multi-Device Attention Inference with TensorRT", "Generating the ONNX
+ * Models", Step 1.]
  *   out        receives the block (set to NULL on failure).
  *   hidden     h = num_heads * head_dim; head_dim 128 for ATTN_F16,
  *              64 or 128 for ATTN_F32.
@@ -169,6 +182,13 @@ attn_status_t attn_block_set_prenorm(attn_block_t *blk, const void *gain, float 
 
 /*
  * attn_block_forward -- y = Block(x) for an activation [seq][batch][hidden].
+ * [Project to Q, K, V, split heads, scaled dot-product attention per head,
+ * concatenate and multiply by W_O: "Tensor Parallelism: Sharding Weights for
+ * Parallel Layer Execution", section 3, steps 1-4; q_scaled and the
+ * (sequence, batch, hidden) activation: "Multi-Device Attention Inference with
+ * TensorRT", "What is hint.json?"; no causal mask: news summary of "Scaling AI
+ * Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+ * Inference Support", context parallelism.]
  *   x, y   device [seq][batch][h] in the block's dtype, 16-byte aligned; x and
  *          y must not overlap. y is not written when taps->qkv_only is set.
  *   seq    0 <= seq*batch <= max_tokens; seq = 0 enqueues nothing.
@@ -188,24 +208,56 @@ attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int6
  * keys/values, all heads: o_part = softmax(q_scaled K^T) V normalised within
  * the block, and its LSE. With the block being all keys this is the
  * AllGather-KV share; with K/V streamed in blocks it is one Ring step.
+ * [A rank keeps its own Q slice and attends to the gathered K/V, or to K/V
+ * streamed in blocks combined by online softmax: news summary of "Scaling AI
+ * Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+ * Inference Support", the three context-parallel implementations; q_scaled
+ * stays local and K/V are gathered: "Multi-Device Attention Inference with
+ * TensorRT", "What is hint.json?".]
  *   num_heads, head_dim, dt  as for the block (d = 128 for ATTN_F16).
  *   q_scaled  element (j,i,c) at q_scaled[j*q_head_stride + i*head_dim + c],
  *             i < sq; already multiplied by 1/sqrt(head_dim).
- *   k         element (j,t,c) at k[j*k_head_stride + t*head_dim + c], t < skv.
- *   v_t       element (j,c,t) at v_t[j*v_head_stride + c*v_row_stride + t]
- *             (V transposed per head: keys contiguous).
+ *   k, v      element (j,t,c) at k[j*kv_head_stride + t*head_dim + c] and
+ *             v[j*kv_head_stride + t*head_dim + c], t < skv (head-major, rows
+ *             of head_dim contiguous elements; both use the one head stride).
  *   o_part    fp32 [H][sq][d] (contiguous), normalised within the block.
  *   lse_part  fp32 [H][sq] (contiguous), natural-log.
- * Pointers 16-byte aligned; head strides and v_row_stride multiples of 8
- * (ATTN_F16) or 4 (ATTN_F32); v_row_stride >= skv. sq = 0 enqueues nothing.
- * skv = 0 writes o_part = 0 and lse_part = -inf (a block with no keys, which
- * carries zero weight in attn_merge_lse).
+ * The attention kernel reads V with keys contiguous, so this call first
+ * transposes V into a V^T staging buffer taken from a library-owned,
+ * stream-ordered device pool (H*d*ATTN_VT_LD(skv) elements, allocated on
+ * `stream` and released on it after the kernels; the pool keeps the memory
+ * for reuse). That pass reads and writes H*skv*d elements more than
+ * attn_partial_forward_vt, which takes V^T directly. Calls on different
+ * streams may overlap.
+ * Pointers 16-byte aligned; head strides multiples of 8 (ATTN_F16) or 4
+ * (ATTN_F32), q_head_stride >= sq*d and kv_head_stride >= skv*d when
+ * num_heads > 1. sq = 0 enqueues nothing. skv = 0 writes o_part = 0 and
+ * lse_part = -inf (a block with no keys, which carries zero weight in
+ * attn_merge_lse). Errors: ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_OOM
+ * (the staging buffer), ATTN_E_HIP.
  */
 attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt,
                                    const void *q_scaled, int64_t sq, int64_t q_head_stride,
-                                   const void *k, int64_t skv, int64_t k_head_stride,
-                                   const void *v_t, int64_t v_head_stride, int64_t v_row_stride,
+                                   const void *k, const void *v, int64_t skv, int64_t kv_head_stride,
                                    float *o_part, float *lse_part, hipStream_t stream);
+
+/*
+ * attn_partial_forward_vt -- attn_partial_forward with V given transposed per
+ * head (keys contiguous), the layout the block's projection writes (the v_t
+ * tap) and the attention kernel reads, so no staging pass and no allocation.
+ * [Same definition and sources as attn_partial_forward.]
+ *   k         element (j,t,c) at k[j*k_head_stride + t*head_dim + c], t < skv.
+ *   v_t       element (j,c,t) at v_t[j*v_head_stride + c*v_row_stride + t]
+ *             (V transposed per head: keys contiguous).
+ * Other arguments, outputs and errors as for attn_partial_forward (no
+ * ATTN_E_OOM). v_row_stride >= skv and a multiple of 8 (ATTN_F16) or 4
+ * (ATTN_F32).
+ */
+attn_status_t attn_partial_forward_vt(int num_heads, int head_dim, attn_dtype_t dt,
+                                      const void *q_scaled, int64_t sq, int64_t q_head_stride,
+                                      const void *k, int64_t skv, int64_t k_head_stride,
+                                      const void *v_t, int64_t v_head_stride, int64_t v_row_stride,
+                                      float *o_part, float *lse_part, hipStream_t stream);
 
 /*
  * attn_heads_forward -- attention of num_heads heads over the full sequence,
@@ -264,6 +316,12 @@ attn_status_t attn_ulysses_unpack_o(int n_ranks, int num_heads, int head_dim, at
  * attn_merge_lse -- combine n_parts partial results of the same query rows
  * by log-sum-exp: with M = max_b lse_b, lse = M + ln sum_b exp(lse_b - M)
  * and o = sum_b exp(lse_b - lse) o_b (online softmax across blocks).
+ * [Blocks of K/V combined by online softmax (Ring Attention): news summary
+ * of "Scaling AI Inference Across Multiple GPUs Using NVIDIA TensorRT with
+ * Multi-Device Inference Support", the three context-parallel
+ * implementations; the output is the concatenation of the heads that W_O
+ * multiplies: "Tensor Parallelism: Sharding Weights for Parallel Layer
+ * Execution", section 3, step 4.]
  * Parts are summed in index order 0..n_parts-1 (deterministic).
  *   o_parts   fp32 [n_parts][H][sq][d] contiguous, each normalised in its block.
  *   lse_parts fp32 [n_parts][H][sq] contiguous.
@@ -324,11 +382,16 @@ attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled, int64_t
 void attn_ring_destroy(attn_ring_t *ring);
 
 /* attn_block_destroy -- synchronise the block's device and free everything
- * the block owns. NULL is a no-op. */
+ * the block owns. NULL is a no-op. [Borrowed resources outlive their user,
+ * as an execution context's communicator must stay valid while the context
+ * lives: news summary of "Scaling AI Inference Across Multiple GPUs Using
+ * NVIDIA TensorRT with Multi-Device Inference Support", the paragraph on
+ * running the engine; the block owns only what create made.] */
 void attn_block_destroy(attn_block_t *blk);
 
 /* attn_last_error -- thread-local, NUL-terminated text for the last non-OK
- * status returned on this thread ("" if none). Valid until the next call. */
+ * status returned on this thread ("" if none). Valid until the next call.
+ * [Library convention: the pages define no error interface.] */
 const char *attn_last_error(void);
 
 #ifdef __cplusplus

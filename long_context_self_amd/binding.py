@@ -7,7 +7,8 @@ unless one is passed). The functions keep the C names:
 * ``attn_block_create`` / ``attn_block_set_prenorm`` / ``attn_block_forward`` /
   ``attn_block_destroy`` (wrapped by the ``AttnBlock`` class),
 * ``attn_block_create_shard`` (tensor-parallel share, ``AttnBlock(..., n_ranks=, rank=)``),
-* ``attn_partial_forward``, ``attn_merge_lse``, ``attn_heads_forward``,
+* ``attn_partial_forward`` (V row-major), ``attn_partial_forward_vt`` (V^T),
+  ``attn_merge_lse``, ``attn_heads_forward``,
 * ``attn_ulysses_gather``, ``attn_ulysses_unpack_o``,
 * ``attn_ring_create`` / ``attn_ring_forward`` / ``attn_ring_destroy`` (the ``AttnRing`` class).
 
@@ -30,7 +31,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_E_INVALID_ARG", 2: "ATTN_E_UNSUPPORTED", 
                 4: "ATTN_E_HIP"}
 
 EXPORTS = ("attn_block_create", "attn_block_create_shard", "attn_block_set_prenorm", "attn_block_forward",
-           "attn_partial_forward", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
+           "attn_partial_forward", "attn_partial_forward_vt", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
            "attn_ulysses_unpack_o", "attn_ring_create", "attn_ring_forward", "attn_ring_destroy",
            "attn_block_destroy", "attn_last_error")
 
@@ -49,7 +50,7 @@ class AttnError(RuntimeError):
 class Taps(ctypes.Structure):
     _fields_ = [("q_scaled", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v_t", ctypes.c_void_p),
                 ("attn_out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("qkv_only", ctypes.c_int),
-                ("events", ctypes.c_void_p)]
+                ("events", ctypes.c_void_p), ("v", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,8 +86,10 @@ def lib() -> ctypes.CDLL:
     L.attn_block_set_prenorm.restype = i32
     L.attn_block_forward.argtypes = [vp, vp, vp, i64, i64, ctypes.POINTER(Taps), vp]
     L.attn_block_forward.restype = i32
-    L.attn_partial_forward.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]
+    L.attn_partial_forward.argtypes = [i32, i32, i32, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp]
     L.attn_partial_forward.restype = i32
+    L.attn_partial_forward_vt.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]
+    L.attn_partial_forward_vt.restype = i32
     L.attn_merge_lse.argtypes = [i32, i32, i32, i64, vp, vp, vp, i32, vp, vp]
     L.attn_merge_lse.restype = i32
     L.attn_block_destroy.argtypes = [vp]
@@ -177,11 +180,19 @@ def attn_block_destroy(handle: int) -> None:
 
 
 def attn_partial_forward(num_heads: int, head_dim: int, q_scaled, sq: int, q_head_stride: int,
-                         k, skv: int, k_head_stride: int, v_t, v_head_stride: int, v_row_stride: int,
-                         o_part, lse_part, dtype: torch.dtype = torch.float16, stream=None) -> None:
+                         k, v, skv: int, kv_head_stride: int, o_part, lse_part,
+                         dtype: torch.dtype = torch.float16, stream=None) -> None:
     _check(lib().attn_partial_forward(num_heads, head_dim, _dtype_code(dtype), _ptr(q_scaled), sq,
-                                      q_head_stride, _ptr(k), skv, k_head_stride, _ptr(v_t), v_head_stride,
-                                      v_row_stride, _ptr(o_part), _ptr(lse_part), _stream(stream)))
+                                      q_head_stride, _ptr(k), _ptr(v), skv, kv_head_stride, _ptr(o_part),
+                                      _ptr(lse_part), _stream(stream)))
+
+
+def attn_partial_forward_vt(num_heads: int, head_dim: int, q_scaled, sq: int, q_head_stride: int,
+                            k, skv: int, k_head_stride: int, v_t, v_head_stride: int, v_row_stride: int,
+                            o_part, lse_part, dtype: torch.dtype = torch.float16, stream=None) -> None:
+    _check(lib().attn_partial_forward_vt(num_heads, head_dim, _dtype_code(dtype), _ptr(q_scaled), sq,
+                                         q_head_stride, _ptr(k), skv, k_head_stride, _ptr(v_t), v_head_stride,
+                                         v_row_stride, _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
 def attn_merge_lse(n_parts: int, num_heads: int, head_dim: int, sq: int, o_parts, lse_parts, o_out,

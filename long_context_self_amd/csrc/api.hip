@@ -207,7 +207,8 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
                                           const attn_taps_t *taps, hipStream_t stream) {
     TapsView tv{};
     if (taps)
-        tv = TapsView{taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->lse, taps->qkv_only, taps->events};
+        tv = TapsView{taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->lse, taps->qkv_only, taps->events,
+                      taps->v};
     Check c = validate_forward(blk == nullptr, blk ? blk->dt : 0, blk ? blk->hidden : 0,
                                blk ? blk->max_tokens : 0, x, y, seq, batch, taps ? &tv : nullptr);
     if (c.status != kOk) return report(c);
@@ -223,6 +224,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
     float *lse = taps ? taps->lse : nullptr;
     const bool qkv_only = taps && taps->qkv_only;
     hipEvent_t *ev = taps ? taps->events : nullptr;
+    void *v_rows = taps ? taps->v : nullptr;  // row-major V tap: transposed back from V^T
 #define MARK(i) \
     if (ev) HIP_TRY("attn_block_forward: hipEventRecord", hipEventRecord(ev[i], stream))
     MARK(0);
@@ -252,6 +254,10 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.q_scale = q_scale;
         g.row_scale = row_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f16(g, stream));
+        if (v_rows)
+            HIP_TRY("attn_block_forward: V tap",
+                    launch_transpose_heads(vt, (int64_t)d * vt_ld, vt_ld, v_rows, (int64_t)S * d, d, H, d, d, S, 2,
+                                           stream));
         MARK(1);
         if (qkv_only) return ATTN_OK;
         FlashArgs fa{};
@@ -325,6 +331,10 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.q_scale = q_scale;
         g.row_scale = row_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f32(g, stream));
+        if (v_rows)
+            HIP_TRY("attn_block_forward: V tap",
+                    launch_transpose_heads(vt, (int64_t)d * vt_ld, vt_ld, v_rows, (int64_t)S * d, d, H, d, d, S, 4,
+                                           stream));
         MARK(1);
         if (qkv_only) return ATTN_OK;
         FlashArgsF32 fa{};
@@ -359,50 +369,6 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         MARK(3);
     }
 #undef MARK
-    return ATTN_OK;
-}
-
-ATTN_API attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
-                                            int64_t sq, int64_t q_head_stride, const void *k, int64_t skv,
-                                            int64_t k_head_stride, const void *v_t, int64_t v_head_stride,
-                                            int64_t v_row_stride, float *o_part, float *lse_part,
-                                            hipStream_t stream) {
-    Check c = validate_partial(num_heads, head_dim, (int)dt, q_scaled, sq, q_head_stride, k, skv, k_head_stride,
-                               v_t, v_head_stride, v_row_stride, o_part, lse_part);
-    if (c.status != kOk) return report(c);
-    if (sq == 0) return ATTN_OK;
-    if (dt == ATTN_F16) {
-        FlashArgs fa{};
-        fa.q = static_cast<const _Float16 *>(q_scaled);
-        fa.k = static_cast<const _Float16 *>(k);
-        fa.vt = static_cast<const _Float16 *>(v_t);
-        fa.q_head_stride = q_head_stride;
-        fa.k_head_stride = k_head_stride;
-        fa.v_head_stride = v_head_stride;
-        fa.v_row_stride = v_row_stride;
-        fa.sq = (int)sq;
-        fa.skv = (int)skv;
-        fa.num_heads = num_heads;
-        fa.o32 = o_part;
-        fa.lse = lse_part;
-        HIP_TRY("attn_partial_forward", launch_flash_fwd_f16(fa, stream));
-    } else {
-        FlashArgsF32 fa{};
-        fa.q = static_cast<const float *>(q_scaled);
-        fa.k = static_cast<const float *>(k);
-        fa.vt = static_cast<const float *>(v_t);
-        fa.q_head_stride = q_head_stride;
-        fa.k_head_stride = k_head_stride;
-        fa.v_head_stride = v_head_stride;
-        fa.v_row_stride = v_row_stride;
-        fa.sq = (int)sq;
-        fa.skv = (int)skv;
-        fa.num_heads = num_heads;
-        fa.head_dim = head_dim;
-        fa.o32 = o_part;
-        fa.lse = lse_part;
-        HIP_TRY("attn_partial_forward", launch_flash_fwd_f32(fa, stream));
-    }
     return ATTN_OK;
 }
 

@@ -31,6 +31,9 @@ struct FlashArgs {
     // blocks), keys [split * split_len, min(skv, (split + 1) * split_len)),
     // and writes its partial o32 / lse at split * H * sq * d / split * H * sq.
     int n_split, split_len;
+    // Non-zero: q holds q_scaled * log2(e) (the block's internal Q), so the
+    // softmax works in base 2 with no per-score multiply.
+    int q_log2e;
 };
 
 struct FlashArgsF32 {
@@ -125,6 +128,16 @@ hipError_t launch_rms_rowscale(const void *x, bool f16, int64_t rows, int h, flo
                                hipStream_t stream);
 hipError_t launch_fold_gain(void *w_qkv, bool f16, int h, int64_t n_out, const void *gain, hipStream_t stream);
 hipError_t launch_seg_copy(SegCopyArgs a, hipStream_t stream);
+// Batched transpose of 2- or 4-byte elements: for every head b < heads,
+// row r < rows and column c < cols, dst[b][c][r] = src[b][r][c], with
+//   src element (b, r, c) at src + b*src_hs + r*src_rs + c,
+//   dst element (b, c, r) at dst + b*dst_hs + c*dst_rs + r (strides in elements).
+// E = 16 / elem_bytes. Each src row must be readable up to round_up(cols, E)
+// elements; each dst row is written for r < rows_out (a multiple of E, >= rows),
+// zeros past rows. Pointers 16-byte aligned and strides multiples of E.
+hipError_t launch_transpose_heads(const void *src, int64_t src_hs, int64_t src_rs, void *dst, int64_t dst_hs,
+                                  int64_t dst_rs, int heads, int64_t rows, int64_t rows_out, int64_t cols,
+                                  int elem_bytes, hipStream_t stream);
 // dst[n][k] = src[k][n] for an [rows][cols] fp16 matrix (dst is [cols][rows]).
 hipError_t launch_transpose_f16(const _Float16 *src, int rows, int cols, int64_t ld_src, _Float16 *dst,
                                 int64_t ld_dst, hipStream_t stream);

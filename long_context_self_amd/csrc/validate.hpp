@@ -78,6 +78,7 @@ struct TapsView {
     const float *lse;
     int qkv_only;
     const void *events;  // array of 4 events; entries are checked by the caller
+    const void *v;
 };
 
 inline Check validate_forward(bool blk_null, int dt, int hidden, int64_t max_tokens, const void *x,
@@ -98,7 +99,7 @@ inline Check validate_forward(bool blk_null, int dt, int hidden, int64_t max_tok
     const int64_t bytes = seq * batch * hidden * elem_size(dt);
     if (y && !qkv_only && overlap(x, bytes, y, bytes)) return fail(kInvalid, "attn_block_forward: x and y overlap");
     if (taps) {
-        const void *p16[4] = {taps->q_scaled, taps->k, taps->v_t, taps->attn_out};
+        const void *p16[5] = {taps->q_scaled, taps->k, taps->v_t, taps->attn_out, taps->v};
         for (const void *p : p16)
             if (p && !aligned(p, 16)) return fail(kInvalid, "attn_block_forward: tap buffers must be 16-byte aligned");
         if (taps->lse && !aligned(taps->lse, 4)) return fail(kInvalid, "attn_block_forward: lse tap misaligned");
@@ -106,37 +107,68 @@ inline Check validate_forward(bool blk_null, int dt, int hidden, int64_t max_tok
     return ok();
 }
 
+// Checks shared by the partial entry points: sizes, q and the outputs.
+inline Check validate_partial_common(const char *what, int num_heads, int head_dim, int dt, const void *q,
+                                     int64_t sq, int64_t qhs, int64_t skv, const float *o_part,
+                                     const float *lse_part) {
+    if (!dtype_known(dt)) return fail(kInvalid, "%s: unknown dtype %d", what, dt);
+    if (num_heads < 1) return fail(kInvalid, "%s: num_heads %d < 1", what, num_heads);
+    if (!head_dim_supported(dt, head_dim))
+        return fail(kUnsupported, "%s: head_dim %d not supported for dtype %d", what, head_dim, dt);
+    if (sq < 0 || skv < 0) return fail(kInvalid, "%s: negative sq or skv", what);
+    if (sq > kMaxTokens || skv > kMaxTokens)
+        return fail(kUnsupported, "%s: sq or skv above %lld", what, (long long)kMaxTokens);
+    if (sq == 0) return ok();
+    if (!q || !o_part || !lse_part) return fail(kInvalid, "%s: q, o_part or lse_part is NULL", what);
+    if (!aligned(q, 16) || !aligned(o_part, 16))
+        return fail(kInvalid, "%s: q and o_part must be 16-byte aligned", what);
+    if (!aligned(lse_part, 4)) return fail(kInvalid, "%s: lse_part misaligned", what);
+    if (qhs < 0) return fail(kInvalid, "%s: negative stride", what);
+    if (qhs % vec_elems(dt))
+        return fail(kInvalid, "%s: head strides must be multiples of %lld", what, (long long)vec_elems(dt));
+    if (num_heads > 1 && qhs < sq * head_dim)
+        return fail(kInvalid, "%s: q_head_stride %lld < sq*head_dim", what, (long long)qhs);
+    return ok();
+}
+
+// attn_partial_forward_vt: K [H][skv][d] and V^T [H][d][v_row_stride].
 inline Check validate_partial(int num_heads, int head_dim, int dt, const void *q, int64_t sq, int64_t qhs,
                               const void *k, int64_t skv, int64_t khs, const void *vt, int64_t vhs,
                               int64_t vrs, const float *o_part, const float *lse_part) {
-    if (!dtype_known(dt)) return fail(kInvalid, "attn_partial_forward: unknown dtype %d", dt);
-    if (num_heads < 1) return fail(kInvalid, "attn_partial_forward: num_heads %d < 1", num_heads);
-    if (!head_dim_supported(dt, head_dim))
-        return fail(kUnsupported, "attn_partial_forward: head_dim %d not supported for dtype %d", head_dim, dt);
-    if (sq < 0 || skv < 0) return fail(kInvalid, "attn_partial_forward: negative sq or skv");
-    if (sq > kMaxTokens || skv > kMaxTokens)
-        return fail(kUnsupported, "attn_partial_forward: sq or skv above %lld", (long long)kMaxTokens);
-    if (sq == 0) return ok();
-    if (!q || !o_part || !lse_part) return fail(kInvalid, "attn_partial_forward: q, o_part or lse_part is NULL");
-    if (skv > 0 && (!k || !vt)) return fail(kInvalid, "attn_partial_forward: k or v_t is NULL");
-    if (!aligned(q, 16) || !aligned(o_part, 16) || (skv > 0 && (!aligned(k, 16) || !aligned(vt, 16))))
-        return fail(kInvalid, "attn_partial_forward: q, k, v_t and o_part must be 16-byte aligned");
-    if (!aligned(lse_part, 4)) return fail(kInvalid, "attn_partial_forward: lse_part misaligned");
+    const char *what = "attn_partial_forward_vt";
+    Check c = validate_partial_common(what, num_heads, head_dim, dt, q, sq, qhs, skv, o_part, lse_part);
+    if (c.status != kOk || sq == 0) return c;
+    if (skv > 0 && (!k || !vt)) return fail(kInvalid, "%s: k or v_t is NULL", what);
+    if (skv > 0 && (!aligned(k, 16) || !aligned(vt, 16)))
+        return fail(kInvalid, "%s: k and v_t must be 16-byte aligned", what);
     const int64_t ve = vec_elems(dt);
-    if (qhs < 0 || khs < 0 || vhs < 0 || vrs < 0)
-        return fail(kInvalid, "attn_partial_forward: negative stride");
-    if (qhs % ve || khs % ve || vhs % ve || vrs % ve)
-        return fail(kInvalid, "attn_partial_forward: head strides and v_row_stride must be multiples of %lld",
-                    (long long)ve);
-    if (num_heads > 1 && qhs < sq * head_dim)
-        return fail(kInvalid, "attn_partial_forward: q_head_stride %lld < sq*head_dim", (long long)qhs);
+    if (khs < 0 || vhs < 0 || vrs < 0) return fail(kInvalid, "%s: negative stride", what);
+    if (khs % ve || vhs % ve || vrs % ve)
+        return fail(kInvalid, "%s: head strides and v_row_stride must be multiples of %lld", what, (long long)ve);
     if (skv > 0) {
-        if (vrs < skv) return fail(kInvalid, "attn_partial_forward: v_row_stride %lld < skv", (long long)vrs);
+        if (vrs < skv) return fail(kInvalid, "%s: v_row_stride %lld < skv", what, (long long)vrs);
         if (vrs > kMaxTokens)  // keeps every in-head V^T offset within 32 bits
-            return fail(kUnsupported, "attn_partial_forward: v_row_stride above %lld", (long long)kMaxTokens);
+            return fail(kUnsupported, "%s: v_row_stride above %lld", what, (long long)kMaxTokens);
         if (num_heads > 1 && (khs < skv * head_dim || vhs < head_dim * vrs))
-            return fail(kInvalid, "attn_partial_forward: k/v head strides smaller than one head");
+            return fail(kInvalid, "%s: k/v head strides smaller than one head", what);
     }
+    return ok();
+}
+
+// attn_partial_forward: K and V both [H][skv][d] with one head stride.
+inline Check validate_partial_rows(const char *what, int num_heads, int head_dim, int dt, const void *q, int64_t sq,
+                                   int64_t qhs, const void *k, const void *v, int64_t skv, int64_t kvhs,
+                                   const float *o_part, const float *lse_part) {
+    Check c = validate_partial_common(what, num_heads, head_dim, dt, q, sq, qhs, skv, o_part, lse_part);
+    if (c.status != kOk || sq == 0) return c;
+    if (skv > 0 && (!k || !v)) return fail(kInvalid, "%s: k or v is NULL", what);
+    if (skv > 0 && (!aligned(k, 16) || !aligned(v, 16)))
+        return fail(kInvalid, "%s: k and v must be 16-byte aligned", what);
+    if (kvhs < 0) return fail(kInvalid, "%s: negative stride", what);
+    if (kvhs % vec_elems(dt))
+        return fail(kInvalid, "%s: head strides must be multiples of %lld", what, (long long)vec_elems(dt));
+    if (skv > 0 && num_heads > 1 && kvhs < skv * head_dim)
+        return fail(kInvalid, "%s: kv_head_stride %lld < skv*head_dim", what, (long long)kvhs);
     return ok();
 }
 

@@ -61,11 +61,22 @@ def to_vt(v: np.ndarray) -> np.ndarray:
 
 
 def partial(q, k, vt, sq, skv, ld, dtype=torch.float16):
-    """attn_partial_forward on contiguous [H,sq,d] q, [H,skv,d] k and
+    """attn_partial_forward_vt on contiguous [H,sq,d] q, [H,skv,d] k and
     [H,d,ld] v_t device tensors -> (o [H,sq,d] fp32, lse [H,sq] fp32)."""
     hh, _, d = q.shape
     o = torch.empty((hh, sq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((hh, sq), dtype=torch.float32, device="cuda")
-    B.attn_partial_forward(hh, d, q, sq, q.stride(0), k, skv, k.stride(0), vt, vt.stride(0), ld, o, lse,
+    B.attn_partial_forward_vt(hh, d, q, sq, q.stride(0), k, skv, k.stride(0), vt, vt.stride(0), ld, o, lse,
                            dtype=dtype)
+    return o, lse
+
+
+def partial_rows(q, k, v, sq, skv, dtype=torch.float16, stream=None):
+    """attn_partial_forward (V row-major) on [H,sq,d] q and [H,*,d] k, v device
+    tensors sharing one head stride -> (o [H,sq,d] fp32, lse [H,sq] fp32)."""
+    hh, _, d = q.shape
+    assert k.stride() == v.stride()
+    o = torch.empty((hh, sq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hh, sq), dtype=torch.float32, device="cuda")
+    B.attn_partial_forward(hh, d, q, sq, q.stride(0), k, v, skv, k.stride(0), o, lse, dtype=dtype, stream=stream)
     return o, lse

@@ -78,6 +78,26 @@ int main() {
     EXPECT(validate_partial(4, 64, kF32, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status == kOk);
     EXPECT(validate_partial(4, 64, kF16, P, 256, 256 * 64, P, 64, 256 * 64, P, 64 * 256, 256, F, F).status ==
            kUnsupported);
+    // partial with row-major V
+    EXPECT(validate_partial_rows("p", 32, 128, kF16, P, 4096, 4096 * 128, P, P, 4096, 32768 * 128, F, F).status ==
+           kOk);
+    EXPECT(validate_partial_rows("p", 32, 128, kF16, P, 4096, 4096 * 128, P, P, 4096, 4000 * 128, F, F).status ==
+           kInvalid);
+    EXPECT(validate_partial_rows("p", 32, 128, kF16, P, 4096, 4096 * 128, P, P, 4096, 4096 * 128 + 4, F, F).status ==
+           kInvalid);
+    EXPECT(validate_partial_rows("p", 32, 128, kF16, P, 4096, 4096 * 128, P, nullptr, 4096, 4096 * 128, F, F)
+               .status == kInvalid);
+    EXPECT(validate_partial_rows("p", 32, 128, kF16, P, 1, 128, nullptr, nullptr, 0, 0, F, F).status == kOk);
+    EXPECT(validate_partial_rows("p", 4, 64, kF32, P, 256, 256 * 64, P, P, 64, 64 * 64, F, F).status == kOk);
+    EXPECT(validate_partial_rows("p", 4, 64, kF32, P, 256, 256 * 64, P, P, 64, 64 * 64 + 2, F, F).status ==
+           kInvalid);
+    EXPECT(validate_partial_rows("p", 4, 128, kF16, P, 256, 256 * 128, P, reinterpret_cast<const char *>(P) + 8, 64,
+                                 64 * 128, F, F).status == kInvalid);
+    EXPECT(validate_partial_rows("p", 4, 128, kF16, P, 256, 256 * 128, P, P, kMaxTokens + 1, 0, F, F).status ==
+           kUnsupported);
+    t.k = nullptr;
+    t.v = reinterpret_cast<const char *>(P) + 4;
+    EXPECT(validate_forward(false, kF16, 4096, 1024, P, nullptr, 16, 1, &t).status == kInvalid);
     // merge
     EXPECT(validate_shard(32, 8, 7).status == kOk);
     EXPECT(validate_shard(32, 1, 0).status == kOk);

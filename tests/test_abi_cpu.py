@@ -128,8 +128,8 @@ def test_partial_rejects(L):
 
     def call(**kw):
         a = dict(args, **kw)
-        return L.attn_partial_forward(a["nh"], a["d"], a["dt"], a["q"], a["sq"], a["qhs"], a["k"], a["skv"],
-                                      a["khs"], a["v"], a["vhs"], a["vrs"], a["o"], a["lse"], None)
+        return L.attn_partial_forward_vt(a["nh"], a["d"], a["dt"], a["q"], a["sq"], a["qhs"], a["k"], a["skv"],
+                                         a["khs"], a["v"], a["vhs"], a["vrs"], a["o"], a["lse"], None)
 
     assert call(d=64) == B.ATTN_E_UNSUPPORTED
     assert call(dt=B.ATTN_F32, d=96) == B.ATTN_E_UNSUPPORTED
@@ -145,6 +145,30 @@ def test_partial_rejects(L):
     big = (1 << 24) + 8
     assert call(vrs=big, vhs=128 * big) == B.ATTN_E_UNSUPPORTED and "v_row_stride" in _err(L)
     assert call(sq=0) == B.ATTN_OK  # nothing to do, nothing enqueued
+
+
+def test_partial_rows_rejects(L):
+    """attn_partial_forward (V row-major [H][skv][d], one K/V head stride)."""
+    args = dict(nh=32, d=128, dt=B.ATTN_F16, q=FAKE, sq=256, qhs=256 * 128, k=FAKE, v=FAKE, skv=512,
+                kvhs=512 * 128, o=FAKE, lse=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.attn_partial_forward(a["nh"], a["d"], a["dt"], a["q"], a["sq"], a["qhs"], a["k"], a["v"], a["skv"],
+                                      a["kvhs"], a["o"], a["lse"], None)
+
+    assert call(d=64) == B.ATTN_E_UNSUPPORTED and "attn_partial_forward:" in _err(L)
+    assert call(dt=B.ATTN_F32, d=96) == B.ATTN_E_UNSUPPORTED
+    assert call(q=None) == B.ATTN_E_INVALID_ARG
+    assert call(v=None) == B.ATTN_E_INVALID_ARG and "k or v is NULL" in _err(L)
+    assert call(k=None) == B.ATTN_E_INVALID_ARG
+    assert call(v=FAKE + 8) == B.ATTN_E_INVALID_ARG and "aligned" in _err(L)
+    assert call(kvhs=500 * 128) == B.ATTN_E_INVALID_ARG and "kv_head_stride" in _err(L)
+    assert call(kvhs=512 * 128 + 4) == B.ATTN_E_INVALID_ARG and "multiples" in _err(L)
+    assert call(sq=-1) == B.ATTN_E_INVALID_ARG
+    assert call(skv=(1 << 24) + 1, kvhs=((1 << 24) + 1) * 128) == B.ATTN_E_UNSUPPORTED
+    assert call(nh=0) == B.ATTN_E_INVALID_ARG
+    assert call(sq=0) == B.ATTN_OK  # nothing to do, nothing enqueued, no staging
 
 
 def test_merge_rejects(L):

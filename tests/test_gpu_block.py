@@ -31,16 +31,18 @@ def _gpu():
     B.lib()
 
 
-def _taps(seq, h, nh, d, dtype, lse=True, qkv_only=False):
+def _taps(seq, h, nh, d, dtype, lse=True, qkv_only=False, v_rows=False):
     t = {
         "q_scaled": torch.empty((nh, seq, d), dtype=dtype, device="cuda"),
         "k": torch.empty((nh, seq, d), dtype=dtype, device="cuda"),
         "v_t": torch.zeros((nh, d, B.vt_ld(seq)), dtype=dtype, device="cuda"),
         "attn_out": torch.empty((seq, h), dtype=dtype, device="cuda"),
         "lse": torch.empty((nh, seq), dtype=torch.float32, device="cuda") if lse else None,
+        "v": torch.empty((nh, seq, d), dtype=dtype, device="cuda") if v_rows else None,
     }
     c = B.Taps(t["q_scaled"].data_ptr(), t["k"].data_ptr(), t["v_t"].data_ptr(), t["attn_out"].data_ptr(),
-               t["lse"].data_ptr() if lse else None, 1 if qkv_only else 0)
+               t["lse"].data_ptr() if lse else None, 1 if qkv_only else 0, None,
+               t["v"].data_ptr() if v_rows else None)
     return t, c
 
 
@@ -55,9 +57,12 @@ def _check_all_rows(seq, h, nh, dtype, rel, mabs):
     d = h // nh
     tdt = torch.float16 if dtype == np.float16 else torch.float32
     blk = _block(ws, nh, seq)
-    t, c = _taps(seq, h, nh, d, tdt)
+    t, c = _taps(seq, h, nh, d, tdt, v_rows=True)
     y = blk.forward(dev(x), taps=c)
     ref = oracle.block_forward(x, *ws, nh, taps=True)
+    # the row-major V tap is the exact transpose of the V^T tap
+    assert torch.equal(t["v"], t["v_t"][:, :, :seq].transpose(1, 2))
+    assert_close(host(t["v"]), ref["v"], rel=rel, mabs=mabs, what="v")
     assert_close(host(y), ref["y"], rel=rel, mabs=mabs, what="y")
     assert_close(host(t["q_scaled"]), ref["q_scaled"], rel=rel, mabs=mabs, what="q_scaled")
     assert_close(host(t["k"]), ref["k"], rel=rel, mabs=mabs, what="k")
@@ -87,7 +92,7 @@ def test_tiny_config_fp32_rank_share_four_chunks():
     o_parts = torch.empty((4, nh, seq, d), dtype=torch.float32, device="cuda")
     lse_parts = torch.empty((4, nh, seq), dtype=torch.float32, device="cuda")
     for b in range(4):
-        B.attn_partial_forward(nh, d, t["q_scaled"], seq, seq * d, t["k"][:, 64 * b:], 64, seq * d,
+        B.attn_partial_forward_vt(nh, d, t["q_scaled"], seq, seq * d, t["k"][:, 64 * b:], 64, seq * d,
                                t["v_t"][:, :, 64 * b:], d * ld, ld, o_parts[b], lse_parts[b], dtype=torch.float32)
     o = torch.empty((seq, h), dtype=torch.float32, device="cuda")
     B.attn_merge_lse(4, nh, d, seq, o_parts, lse_parts, o, torch.float32)
@@ -154,9 +159,13 @@ def test_config_seq8192_hidden8192():
 
 
 def _rank_share(x, ws, seq, h, nh, ranks=8, check_ranks=(0, 7)):
+    """Rank r's share: per K/V block, attn_partial_forward on row-major K/V
+    (the k and v taps) and attn_partial_forward_vt on the v_t tap -- equal bit
+    for bit -- then the LSE merge; and the same chunk against all keys in one
+    call."""
     d = h // nh
     blk = _block(ws, nh, seq)
-    t, c = _taps(seq, h, nh, d, torch.float16, lse=False, qkv_only=True)
+    t, c = _taps(seq, h, nh, d, torch.float16, lse=False, qkv_only=True, v_rows=True)
     blk.forward(dev(x), taps=c)
     ld = B.vt_ld(seq)
     chunk = seq // ranks
@@ -165,16 +174,21 @@ def _rank_share(x, ws, seq, h, nh, ranks=8, check_ranks=(0, 7)):
         q = t["q_scaled"][:, r * chunk:]
         o_parts = torch.empty((ranks, nh, chunk, d), dtype=torch.float32, device="cuda")
         lse_parts = torch.empty((ranks, nh, chunk), dtype=torch.float32, device="cuda")
+        o_rows = torch.empty_like(o_parts)
+        lse_rows = torch.empty_like(lse_parts)
         for b in range(ranks):
-            B.attn_partial_forward(nh, d, q, chunk, seq * d, t["k"][:, b * chunk:], chunk, seq * d,
-                                   t["v_t"][:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b])
+            B.attn_partial_forward_vt(nh, d, q, chunk, seq * d, t["k"][:, b * chunk:], chunk, seq * d,
+                                      t["v_t"][:, :, b * chunk:], d * ld, ld, o_parts[b], lse_parts[b])
+            B.attn_partial_forward(nh, d, q, chunk, seq * d, t["k"][:, b * chunk:], t["v"][:, b * chunk:], chunk,
+                                   seq * d, o_rows[b], lse_rows[b])
+        assert torch.equal(o_rows, o_parts) and torch.equal(lse_rows, lse_parts), "row-major V differs from V^T"
         o = torch.empty((chunk, h), dtype=torch.float16, device="cuda")
         lse = torch.empty((nh, chunk), dtype=torch.float32, device="cuda")
         B.attn_merge_lse(ranks, nh, d, chunk, o_parts, lse_parts, o, torch.float16, lse)
         # AllGather-KV share: one call over all keys
         o1 = torch.empty((1, nh, chunk, d), dtype=torch.float32, device="cuda")
         l1 = torch.empty((1, nh, chunk), dtype=torch.float32, device="cuda")
-        B.attn_partial_forward(nh, d, q, chunk, seq * d, t["k"], seq, seq * d, t["v_t"], d * ld, ld, o1[0], l1[0])
+        B.attn_partial_forward_vt(nh, d, q, chunk, seq * d, t["k"], seq, seq * d, t["v_t"], d * ld, ld, o1[0], l1[0])
         o_one = torch.empty((chunk, h), dtype=torch.float16, device="cuda")
         B.attn_merge_lse(1, nh, d, chunk, o1, l1, o_one, torch.float16)
         split_vs_one = rel_l2(host(o), host(o_one))
@@ -231,21 +245,23 @@ def test_six_stack_small_all_rows():
     assert_close(host(outs[-1]), ref, what="6-stack output")
 
 
+@pytest.mark.timeout(900)
 def test_config_six_stack_seq32768():
+    """Every layer of the 6-block stack at seq 32768, teacher-forced: layer l's
+    oracle input is the GPU's own fp16 output of layer l-1 (x for layer 0),
+    K and V over all 32768 rows, and layer l's GPU output is compared on
+    sampled rows at the block's gates."""
     seq, h, nh = 32768, 4096, 32
-    say("6-stack S=32768: layer 0 on sampled rows; later layers by properties")
+    say("6-stack S=32768: every layer teacher-forced on the previous layer's GPU output, sampled rows")
     x, layers = block_inputs(seq, h, 6, dtype=np.float16, seed=0)
     outs = _stack(x, layers, nh, seq)
-    rows = sample_rows(seq, 128, seed=0)
-    y0 = host(outs[0][rows])
-    ref0 = oracle.block_forward(x, *layers[0], nh, rows=rows)
-    assert_close(y0, ref0, what="layer 0")
-    for i, o in enumerate(outs):
-        assert torch.isfinite(o).all(), f"layer {i} has non-finite values"
-    # With these weight statistics every layer after the second maps nearly
-    # identical rows to nearly identical rows; the oracle shows the same at
-    # small seq (test_six_stack_small_all_rows checks the values there).
-    last = host(outs[-1][rows])
-    spread = np.linalg.norm(last - last.mean(0)) / np.linalg.norm(last)
-    say(f"  final-layer relative row spread {spread:.3e}")
-    assert spread < 1e-2
+    rows = sample_rows(seq, 128, seed=0, must=[seq // 8 * r for r in range(9)])
+    prev = x
+    for li, (o, ws) in enumerate(zip(outs, layers)):
+        got = host(o[rows])
+        ref = oracle.block_forward(prev, *ws, nh, rows=rows)
+        spread = np.linalg.norm(got - got.mean(0)) / np.linalg.norm(got)
+        say(f"  layer {li}: relative row spread of the GPU output {spread:.3e}")
+        assert_close(got, ref, what=f"layer {li} (input: {'x' if li == 0 else f'GPU layer {li - 1}'})")
+        prev = o.cpu().numpy()  # the exact fp16 values the next GPU layer read
+    del outs

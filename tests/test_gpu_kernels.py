@@ -1,7 +1,9 @@
-"""GPU parity of the attention kernel (attn_partial_forward) and the LSE merge
-(attn_merge_lse) against the fp64 oracle, at sizes that span several tiles
-with ragged tails, plus the method's degenerate cases and the GPU-only
-properties (split-merge vs unsplit, row-chunk bit-exactness, determinism)."""
+"""GPU parity of the attention kernel (attn_partial_forward_vt, and
+attn_partial_forward with V row-major) and the LSE merge (attn_merge_lse)
+against the fp64 oracle, at sizes that span several tiles with ragged tails,
+plus the method's degenerate cases and the GPU-only properties (split-merge vs
+unsplit, row-chunk bit-exactness, determinism, row-major V = V^T bit for
+bit)."""
 
 from __future__ import annotations
 
@@ -13,8 +15,8 @@ import oracle
 from long_context_self_amd import binding as B
 from long_context_self_amd.synthetic import attention_inputs
 
-from .gpu_util import (REL_L2_F16, REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, max_abs, partial, rel_l2,
-                       say, to_vt)
+from .gpu_util import (REL_L2_F16, REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, max_abs, partial,
+                       partial_rows, rel_l2, say, to_vt)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +101,7 @@ def test_partial_empty_kv_block():
     q = dev(attention_inputs(h, sq, 1, d)[0])
     o = torch.full((h, sq, d), 7.0, dtype=torch.float32, device="cuda")
     lse = torch.zeros((h, sq), dtype=torch.float32, device="cuda")
-    B.attn_partial_forward(h, d, q, sq, q.stride(0), None, 0, 0, None, 0, 0, o, lse)
+    B.attn_partial_forward_vt(h, d, q, sq, q.stride(0), None, 0, 0, None, 0, 0, o, lse)
     assert np.all(host(o) == 0.0)
     assert np.all(np.isneginf(host(lse)))
 
@@ -210,7 +212,7 @@ def test_partials_on_two_streams_match_one_stream():
             st.wait_event(fork)
         for b in range(n):
             st = streams[b % len(streams)]
-            B.attn_partial_forward(h, d, qd, sq, qd.stride(0), kd[:, b * blk:], blk, kd.stride(0), vt[:, :, b * blk:],
+            B.attn_partial_forward_vt(h, d, qd, sq, qd.stride(0), kd[:, b * blk:], blk, kd.stride(0), vt[:, :, b * blk:],
                                    vt.stride(0), ld, o[b], lse[b], stream=st.cuda_stream)
         for st in streams:
             join = torch.cuda.Event()
@@ -261,3 +263,81 @@ def test_tiny_config_split_into_four_chunks_fp32():
     assert_close(got, o_ref, rel=REL_L2_F32, mabs=1e-5, what="tiny merged vs oracle")
     assert_close(host(lse_m), lse_ref, rel=REL_L2_F32, mabs=1e-5, what="tiny merged lse")
     assert rel_l2(got, host(o_full)) <= REL_L2_SPLIT
+
+
+# ------------------------------------------------ attn_partial_forward, V row-major
+@pytest.mark.parametrize("h,sq,skv,d,dt", [(2, 300, 1, 128, np.float16), (3, 257, 63, 128, np.float16),
+                                           (1, 64, 65, 128, np.float16), (2, 500, 1000, 128, np.float16),
+                                           (4, 256, 4100, 128, np.float16), (4, 256, 300, 64, np.float32),
+                                           (2, 100, 77, 128, np.float32)])
+def test_partial_rows_vs_oracle_and_vt(h, sq, skv, d, dt):
+    """V given row-major [H,skv,d]: within the gates of the oracle, and bit for
+    bit the V^T entry point on the same values (the staging transpose moves
+    data only; the attention kernel is the same)."""
+    say(f"partial rows H={h} sq={sq} skv={skv} d={d} {np.dtype(dt).name}")
+    q, k, v = attention_inputs(h, sq, skv, d, dtype=dt, seed=20 + skv)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o, lse = partial_rows(qd, kd, vd, sq, skv, dtype=tdt)
+    vt = to_vt(v)
+    o_t, lse_t = partial(qd, kd, dev(vt), sq, skv, vt.shape[2], dtype=tdt)
+    assert torch.equal(o, o_t) and torch.equal(lse, lse_t), "row-major V differs from V^T"
+    o_ref, lse_ref = oracle.partial_attention(q, k, v)
+    rel, mabs = (REL_L2_F16, 2e-2) if dt == np.float16 else (REL_L2_F32, 1e-5)
+    assert_close(host(o), o_ref, rel=rel, mabs=mabs, what="o_part (V rows)")
+    assert_close(host(lse), lse_ref, rel=rel, mabs=mabs, what="lse_part (V rows)")
+
+
+def test_partial_rows_strided_heads_and_empty_block():
+    """K/V as views into a longer sequence (head stride > skv*d, as for one
+    block of a gathered K/V), and a block with no keys."""
+    say("partial rows: strided head views, empty block")
+    h, sq, s_all, d = 3, 200, 1500, 128
+    q, k, v = attention_inputs(h, sq, s_all, d, seed=31)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    a, b = 448, 1203
+    o, lse = partial_rows(qd, kd[:, a:], vd[:, a:], sq, b - a)
+    o_ref, lse_ref = oracle.partial_attention(q, k[:, a:b], v[:, a:b])
+    assert_close(host(o), o_ref, what="o_part strided")
+    assert_close(host(lse), lse_ref, what="lse strided")
+    o0 = torch.full((h, sq, d), 7.0, dtype=torch.float32, device="cuda")
+    l0 = torch.zeros((h, sq), dtype=torch.float32, device="cuda")
+    B.attn_partial_forward(h, d, qd, sq, qd.stride(0), None, None, 0, 0, o0, l0)
+    assert torch.all(o0 == 0) and torch.all(torch.isneginf(l0))
+
+
+def test_partial_rows_on_two_streams_match_one_stream():
+    """Each call's V^T staging is taken from and returned to a stream-ordered
+    pool, so row-major partials enqueued alternately on two streams equal the
+    same calls on one stream bit for bit."""
+    say("row-major partials on two streams")
+    h, sq, skv, d, n = 4, 512, 4096, 128, 4
+    q, k, v = attention_inputs(h, sq, skv, d, seed=13)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    blk = skv // n
+
+    def run(streams):
+        o = torch.empty((n, h, sq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((n, h, sq), dtype=torch.float32, device="cuda")
+        main = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        for st in streams:
+            st.wait_event(fork)
+        for b in range(n):
+            st = streams[b % len(streams)]
+            B.attn_partial_forward(h, d, qd, sq, qd.stride(0), kd[:, b * blk:], vd[:, b * blk:], blk, kd.stride(0),
+                                   o[b], lse[b], stream=st.cuda_stream)
+        for st in streams:
+            join = torch.cuda.Event()
+            join.record(st)
+            main.wait_event(join)
+        torch.cuda.synchronize()
+        return o, lse
+
+    one = run([torch.cuda.current_stream()])
+    two = run([torch.cuda.current_stream(), torch.cuda.Stream()])
+    for a, b2 in zip(one, two):
+        assert torch.equal(a, b2)
+    o_ref, lse_ref = oracle.partial_attention(q, k[:, :blk], v[:, :blk])
+    assert_close(host(one[0][0]), o_ref, what="block 0 o_part")

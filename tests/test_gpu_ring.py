@@ -54,7 +54,7 @@ def _sequential(q, sq, kb, vb, lens, hh, d, dtype=torch.float16):
         kd = kb[b].cuda() if n else None
         vd = vb[b].cuda() if n else None
         ld = B.vt_ld(n)
-        B.attn_partial_forward(hh, d, q, sq, sq * d, kd, n, n * d, vd, d * ld, ld, o_parts[b], lse_parts[b],
+        B.attn_partial_forward_vt(hh, d, q, sq, sq * d, kd, n, n * d, vd, d * ld, ld, o_parts[b], lse_parts[b],
                                dtype=dtype)
     o = torch.empty((sq, hh * d), dtype=dtype, device="cuda")
     lse = torch.empty((hh, sq), dtype=torch.float32, device="cuda")
