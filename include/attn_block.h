@@ -260,6 +260,30 @@ attn_status_t attn_partial_forward_vt(int num_heads, int head_dim, attn_dtype_t 
                                       float *o_part, float *lse_part, hipStream_t stream);
 
 /*
+ * attn_partial_forward_noalloc -- attn_partial_forward for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the V^T staging lives in a fixed
+ * 64 MiB device array of the library instead of the stream-ordered pool, and
+ * the call makes no allocation of any kind.
+ *   Arguments, layouts and results: as attn_partial_forward (bit-identical
+ *   output).
+ *   Limit: num_heads * head_dim * ATTN_VT_LD(skv) * element size <= 64 MiB
+ *   (e.g. 32 heads of 128 in fp16: skv <= 8192); larger calls return
+ *   ATTN_E_UNSUPPORTED, enqueue nothing, and should use attn_partial_forward.
+ *   Each GPU the library runs on holds its own copy of the array until the
+ *   process ends; its device address is looked up once per device, on the
+ *   first call made with that device current.
+ *   All calls on one GPU share that GPU's array: calls that overlap in time
+ *   on one GPU (two streams, or two host threads) race on it. Calls ordered on
+ *   one stream do not.
+ * Errors: those of attn_partial_forward except ATTN_E_OOM.
+ */
+attn_status_t attn_partial_forward_noalloc(int num_heads, int head_dim, attn_dtype_t dt,
+                                           const void *q_scaled, int64_t sq, int64_t q_head_stride,
+                                           const void *k, const void *v, int64_t skv, int64_t kv_head_stride,
+                                           float *o_part, float *lse_part, hipStream_t stream);
+
+/*
  * attn_heads_forward -- attention of num_heads heads over the full sequence,
  * output token-major: o[i][j*d + c] for row i, head j. This is the block's
  * attention step on its own; under Ulysses context parallelism a rank runs it

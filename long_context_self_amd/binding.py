@@ -8,6 +8,7 @@ unless one is passed). The functions keep the C names:
   ``attn_block_destroy`` (wrapped by the ``AttnBlock`` class),
 * ``attn_block_create_shard`` (tensor-parallel share, ``AttnBlock(..., n_ranks=, rank=)``),
 * ``attn_partial_forward`` (V row-major), ``attn_partial_forward_vt`` (V^T),
+  ``attn_partial_forward_noalloc`` (V row-major, fixed staging, no allocation),
   ``attn_merge_lse``, ``attn_heads_forward``,
 * ``attn_ulysses_gather``, ``attn_ulysses_unpack_o``,
 * ``attn_ring_create`` / ``attn_ring_forward`` / ``attn_ring_destroy`` (the ``AttnRing`` class).
@@ -31,7 +32,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_E_INVALID_ARG", 2: "ATTN_E_UNSUPPORTED", 
                 4: "ATTN_E_HIP"}
 
 EXPORTS = ("attn_block_create", "attn_block_create_shard", "attn_block_set_prenorm", "attn_block_forward",
-           "attn_partial_forward", "attn_partial_forward_vt", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
+           "attn_partial_forward", "attn_partial_forward_vt", "attn_partial_forward_noalloc", "attn_merge_lse", "attn_heads_forward", "attn_ulysses_gather",
            "attn_ulysses_unpack_o", "attn_ring_create", "attn_ring_forward", "attn_ring_destroy",
            "attn_block_destroy", "attn_last_error")
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.attn_block_forward.restype = i32
     L.attn_partial_forward.argtypes = [i32, i32, i32, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp]
     L.attn_partial_forward.restype = i32
+    L.attn_partial_forward_noalloc.argtypes = [i32, i32, i32, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp]
+    L.attn_partial_forward_noalloc.restype = i32
     L.attn_partial_forward_vt.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, vp, vp]
     L.attn_partial_forward_vt.restype = i32
     L.attn_merge_lse.argtypes = [i32, i32, i32, i64, vp, vp, vp, i32, vp, vp]
@@ -185,6 +188,14 @@ def attn_partial_forward(num_heads: int, head_dim: int, q_scaled, sq: int, q_hea
     _check(lib().attn_partial_forward(num_heads, head_dim, _dtype_code(dtype), _ptr(q_scaled), sq,
                                       q_head_stride, _ptr(k), _ptr(v), skv, kv_head_stride, _ptr(o_part),
                                       _ptr(lse_part), _stream(stream)))
+
+
+def attn_partial_forward_noalloc(num_heads: int, head_dim: int, q_scaled, sq: int, q_head_stride: int,
+                                 k, v, skv: int, kv_head_stride: int, o_part, lse_part,
+                                 dtype: torch.dtype = torch.float16, stream=None) -> None:
+    _check(lib().attn_partial_forward_noalloc(num_heads, head_dim, _dtype_code(dtype), _ptr(q_scaled), sq,
+                                              q_head_stride, _ptr(k), _ptr(v), skv, kv_head_stride, _ptr(o_part),
+                                              _ptr(lse_part), _stream(stream)))
 
 
 def attn_partial_forward_vt(num_heads: int, head_dim: int, q_scaled, sq: int, q_head_stride: int,

@@ -2,7 +2,8 @@
 // K/V block, all heads): attn_partial_forward takes V row-major [H][skv][d],
 // attn_partial_forward_vt takes V transposed per head. Both end in the same
 // attention kernels; the row-major form first transposes V into a staging
-// buffer from a library-owned stream-ordered pool.
+// buffer from a library-owned stream-ordered pool, and
+// attn_partial_forward_noalloc stages it in a fixed device array instead.
 //
 // Definition: a rank keeps its own Q slice and attends to the gathered K/V,
 // or to K/V streamed in blocks whose normalised partials and LSEs are
@@ -12,6 +13,7 @@
 // Inference with TensorRT", "What is hint.json?": q_scaled stays local).
 
 #include <cstdint>
+#include <cstdio>
 #include <mutex>
 
 #include "attn_block.h"
@@ -111,7 +113,59 @@ hipError_t staging_pool(hipMemPool_t *out) {
     return p.err;
 }
 
+// Fixed staging for attn_partial_forward_noalloc, for callers that cannot
+// allocate. Each device the library runs on holds its own copy of this array
+// from the time the library's code is loaded on it until the process ends.
+// In host code `scratch` names a host-side stand-in, never device memory: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+struct ScratchAddr {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// Device address of this device's `scratch` (the device must be current).
+hipError_t scratch_ptr(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchAddr &s = g_scratch[dev];
+    std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    *out = s.ptr;
+    return s.err;
+}
+
 }  // namespace
+
+ATTN_API attn_status_t attn_partial_forward_noalloc(int num_heads, int head_dim, attn_dtype_t dt,
+                                                    const void *q_scaled, int64_t sq, int64_t q_head_stride,
+                                                    const void *k, const void *v, int64_t skv,
+                                                    int64_t kv_head_stride, float *o_part, float *lse_part,
+                                                    hipStream_t stream) {
+    const char *what = "attn_partial_forward_noalloc";
+    Check c = validate_partial_rows(what, num_heads, head_dim, (int)dt, q_scaled, sq, q_head_stride, k, v, skv,
+                                    kv_head_stride, o_part, lse_part);
+    if (c.status != kOk) return report(c);
+    const size_t bytes = (size_t)num_heads * head_dim * ATTN_VT_LD(skv) * elem_size((int)dt);
+    if (bytes > kScratchBytes) {
+        char msg[256];
+        std::snprintf(msg, sizeof(msg),
+                      "%s: V^T staging needs %zu bytes (num_heads * head_dim * ATTN_VT_LD(skv) elements), above the "
+                      "fixed %zu-byte scratch; use attn_partial_forward",
+                      what, bytes, kScratchBytes);
+        return set_error(kUnsupported, msg);
+    }
+    if (sq == 0) return ATTN_OK;
+    void *vt = nullptr;
+    HIP_TRY("attn_partial_forward_noalloc: scratch address", scratch_ptr(&vt));
+    return enqueue_partial_rows(what, num_heads, head_dim, (int)dt, q_scaled, sq, q_head_stride, k, v, skv,
+                                kv_head_stride, vt, o_part, lse_part, stream);
+}
 
 ATTN_API attn_status_t attn_partial_forward_vt(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
                                                int64_t sq, int64_t q_head_stride, const void *k, int64_t skv,

@@ -171,6 +171,24 @@ def test_partial_rows_rejects(L):
     assert call(sq=0) == B.ATTN_OK  # nothing to do, nothing enqueued, no staging
 
 
+def test_partial_noalloc_rejects(L):
+    """attn_partial_forward_noalloc: the checks of attn_partial_forward, and
+    calls whose V^T staging exceeds the fixed 64 MiB are refused before any
+    HIP call."""
+    def call(nh=32, d=128, dt=B.ATTN_F16, sq=256, skv=4096, kvhs=None, v=FAKE):
+        kvhs = skv * d if kvhs is None else kvhs
+        return L.attn_partial_forward_noalloc(nh, d, dt, FAKE, sq, sq * d, FAKE, v, skv, kvhs, FAKE, FAKE, None)
+
+    assert call(skv=8193) == B.ATTN_E_UNSUPPORTED and "64" in _err(L) and "scratch" in _err(L)
+    assert call(nh=64, skv=4097) == B.ATTN_E_UNSUPPORTED
+    assert call(dt=B.ATTN_F32, d=128, skv=4097) == B.ATTN_E_UNSUPPORTED
+    assert call(skv=8193, sq=0) == B.ATTN_E_UNSUPPORTED  # the limit applies even with no query rows
+    assert call(v=None) == B.ATTN_E_INVALID_ARG and "attn_partial_forward_noalloc" in _err(L)
+    assert call(d=64) == B.ATTN_E_UNSUPPORTED
+    assert call(kvhs=4000 * 128) == B.ATTN_E_INVALID_ARG
+    assert call(sq=0) == B.ATTN_OK
+
+
 def test_merge_rejects(L):
     assert L.attn_merge_lse(0, 32, 128, 16, FAKE, FAKE, FAKE, B.ATTN_F16, None, None) == B.ATTN_E_INVALID_ARG
     assert L.attn_merge_lse(8, 32, 96, 16, FAKE, FAKE, FAKE, B.ATTN_F16, None, None) == B.ATTN_E_UNSUPPORTED
