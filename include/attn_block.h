@@ -72,10 +72,14 @@ typedef struct attn_block attn_block_t;
 
 /*
  * Optional taps of attn_block_forward: caller-owned device buffers that
- * replace the block's internal intermediates (so tapping costs no copy).
+ * receive the block's intermediates. k, v_t, attn_out and lse replace the
+ * block's internal buffers (tapping them costs no copy); taps never change y.
  * Every field may be NULL. Layouts, with S = seq, H = heads, d = head_dim,
  * h = H*d, elements of the block's dtype unless noted:
  *   q_scaled  [H][S][d]   q_scaled = (X W_Q)/sqrt(d), head j = columns j*d..
+ *             (fp16 blocks keep their own Q with an extra factor log2(e), the
+ *             base change of the softmax's exponential, so this tap costs one
+ *             more write of S*h elements from the projection's epilogue)
  *   k         [H][S][d]   K = X W_K, head-major
  *   v_t       [H][d][ATTN_VT_LD(S)]  V = X W_V transposed per head (keys
  *             contiguous); columns S..ld-1 of each row are padding

@@ -53,6 +53,7 @@ namespace {
 constexpr int kFillWorkgroups = 512;
 constexpr int kMaxSplit = 4;
 constexpr int kFlashRows = 256;  // query rows per attention workgroup
+constexpr double kLog2eD = 1.4426950408889634;
 
 int64_t attn_workgroups(int heads, int64_t seq) { return heads * ((seq + kFlashRows - 1) / kFlashRows); }
 
@@ -217,6 +218,10 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
     const int h = blk->hidden, d = blk->head_dim, H = blk->heads, wd = blk->width;
     const int64_t vt_ld = ATTN_VT_LD(S);
     const float q_scale = (float)(1.0 / std::sqrt((double)d));
+    // fp16: the block's own Q holds q_scaled * log2(e) (one rounding from the
+    // fp32 accumulator, like q_scaled itself), so its attention needs no
+    // per-score multiply; a q_scaled tap gets the plain q_scaled in addition.
+    const float q_scale_log2e = (float)(kLog2eD / std::sqrt((double)d));
     void *q = (taps && taps->q_scaled) ? taps->q_scaled : blk->ws_q;
     void *k = (taps && taps->k) ? taps->k : blk->ws_k;
     void *vt = (taps && taps->v_t) ? taps->v_t : blk->ws_vt;
@@ -245,14 +250,16 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         g.N = 3 * wd;
         g.K = h;
         g.mode = kQkv;
-        g.q = static_cast<_Float16 *>(q);
+        g.q = static_cast<_Float16 *>(blk->ws_q);
         g.k = static_cast<_Float16 *>(k);
         g.vt = static_cast<_Float16 *>(vt);
         g.vt_ld = vt_ld;
         g.hidden = wd;
         g.head_dim = d;
-        g.q_scale = q_scale;
+        g.q_scale = q_scale_log2e;
         g.row_scale = row_scale;
+        g.q_tap = (taps && taps->q_scaled) ? static_cast<_Float16 *>(taps->q_scaled) : nullptr;
+        g.q_tap_scale = q_scale;
         HIP_TRY("attn_block_forward: QKV projection", launch_gemm_f16(g, stream));
         if (v_rows)
             HIP_TRY("attn_block_forward: V tap",
@@ -262,6 +269,7 @@ ATTN_API attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void
         if (qkv_only) return ATTN_OK;
         FlashArgs fa{};
         fa.q = g.q;
+        fa.q_log2e = 1;
         fa.k = g.k;
         fa.vt = g.vt;
         fa.q_head_stride = (int64_t)S * d;

@@ -200,12 +200,17 @@ __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<
 
 // P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
 // pf[ks] holds keys 32(ks / 2) + 16h + 8(ks % 2) + 0..7 of the lane's query.
+// PRE: the scores are already (S - m) log2(e) -- Q carries the log2(e)
+// factor and the first S MFMA starts from -m (see the kernel) -- so P is one
+// exp2 per score; otherwise one FMA per score maps S to that argument.
+template <bool PRE>
 __device__ __forceinline__ void exp_and_pack(const floatx16 (&sc)[2], half8 (&pf)[4], float mneg) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            pf[2 * kb + (i >> 3)][i & 7] = (half_t)__builtin_amdgcn_exp2f(fmaf(sc[kb][i], kLog2e, mneg));
+            pf[2 * kb + (i >> 3)][i & 7] =
+                (half_t)__builtin_amdgcn_exp2f(PRE ? sc[kb][i] : fmaf(sc[kb][i], kLog2e, mneg));
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -259,16 +264,37 @@ __device__ __forceinline__ void update_max(float mt, float &m_run, float &l_run,
     }
 }
 
+// The same for PRE scores, which are relative to the reference already
+// (log2 units): mt is the row max of S - m. Where it exceeds 8 the reference
+// moves up by mt, and O, the sum, the pending scores and the accumulator
+// start value -m of later tiles follow it.
+__device__ __forceinline__ void update_max_rel(float mt, float &m_run, float &l_run, floatx16 (&o)[4],
+                                               floatx16 (&s)[2], floatx16 &negm) {
+    const bool need = mt > 8.0f;
+    if (__ballot(need)) {
+        const float delta = need ? mt : 0.0f;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        m_run += delta;
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
+        negm = -m_run;
+    }
+}
+
 // Steady step t: every tile it touches is full, stage t+3 exists and is
 // full, and step t+1 starts with S_{t+2} MFMAs. fr holds this step's first
 // RA operands on entry and the next step's on exit.
+template <bool PRE>
 __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
                                             floatx16 (&o)[4], const half8 (&qf)[8], half8 (&fr)[RA],
-                                            float &m_run, float &l_run) {
+                                            float &m_run, float &l_run, floatx16 &negm) {
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
     half8 pf[4];
-    exp_and_pack(sc, pf, -m_run * kLog2e);
+    exp_and_pack<PRE>(sc, pf, -m_run * kLog2e);
 #pragma unroll
     for (int n = 0; n < 32; ++n) {
         const half8 a = fr[n % RA];
@@ -280,27 +306,31 @@ __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[
         if (n == 20) issue_v_full(c, t + 3, t + 3);
         if (n < 16) {
             const int kk = n >> 1, kb = n & 1;
-            sn[kb] = mfma32(a, qf[kk], kk == 0 ? floatx16{} : sn[kb]);
+            sn[kb] = mfma32(a, qf[kk], kk == 0 ? (PRE ? negm : floatx16{}) : sn[kb]);
         } else {
             const int mb = (n - 16) & 3, ks = (n - 16) >> 2;
             o[mb] = mfma32(a, pf[ks], o[mb]);
         }
     }
     l_run += row_sum(pf);
-    update_max(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o);
+    if (PRE)
+        update_max_rel(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o, sn, negm);
+    else
+        update_max(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
     barrier_no_fence();
 }
 
 // Any step t (the last few of the loop): the same work with every condition
 // checked, and without reading ahead into the next step.
+template <bool PRE>
 __device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
                                              floatx16 (&o)[4], const half8 (&qf)[8], float &m_run,
-                                             float &l_run) {
+                                             float &l_run, floatx16 &negm) {
     const int inflight = issue_stage(c, t + 3);
     const half_t *cur = c.rl + (t & 3) * SLOT;
     half8 pf[4];
-    exp_and_pack(sc, pf, -m_run * kLog2e);
+    exp_and_pack<PRE>(sc, pf, -m_run * kLog2e);
     const bool has_s = t + 1 < c.T;
     if (has_s) {
         half8 fa[16];
@@ -309,7 +339,7 @@ __device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             const int kk = n >> 1, kb = n & 1;
-            sn[kb] = mfma32(fa[n], qf[kk], kk == 0 ? floatx16{} : sn[kb]);
+            sn[kb] = mfma32(fa[n], qf[kk], kk == 0 ? (PRE ? negm : floatx16{}) : sn[kb]);
         }
     }
     {
@@ -324,7 +354,10 @@ __device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)
         const int key0 = (t + 1) * BN;
         const float mt = (key0 + BN <= c.skv) ? row_max<false>(sn, key0, c.skv, c.lane >> 5)
                                                : row_max<true>(sn, key0, c.skv, c.lane >> 5);
-        update_max(mt, m_run, l_run, o);
+        if (PRE)
+            update_max_rel(mt, m_run, l_run, o, sn, negm);
+        else
+            update_max(mt, m_run, l_run, o);
         wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
         barrier_no_fence();
     }
@@ -345,15 +378,20 @@ __device__ __forceinline__ void swap_s(floatx16 (&a)[2], floatx16 (&b)[2]) {
 // stage t-1 used (all of whose reads finished before the barrier that ended
 // step t-1) and ends by waiting for stage t+2 and a barrier, so step t+1 may
 // read stage t+1's operands ahead of that barrier.
-__global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+//
+// PRE (set when q holds q_scaled * log2(e), as the block's projection writes
+// it): the scores come out of the S MFMAs already as (S - m) log2(e) -- the
+// log2(e) factor rides in Q and the first MFMA of each S chain starts from
+// the accumulator value -m (negm) instead of 0 -- so the softmax needs no
+// per-score FMA; m_run is then kept in log2 units.
+template <bool PRE>
+__device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int h = lane >> 5;
 
     const int nqb = (a.sq + BQ - 1) / BQ;
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int per_split = nqb * a.num_heads;
     const int split = a.n_split > 1 ? work / per_split : 0;
     const int head = (work - split * per_split) / nqb;
@@ -374,6 +412,7 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) o[mb] = floatx16{};
     float m_run = -INFINITY, l_run = 0.0f;
+    floatx16 negm = floatx16{};  // PRE: accumulator start value -m of the S MFMAs
 
     Ctx c;
     c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D);
@@ -406,7 +445,15 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
             }
         }
         const float mt = (BN <= skv) ? row_max<false>(sa, 0, skv, h) : row_max<true>(sa, 0, skv, h);
-        update_max(mt, m_run, l_run, o);
+        if (PRE) {
+            // the first tile sets the reference: S_0 came out relative to 0
+            m_run = mt;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[kb] -= mt;
+            negm = -mt;
+        } else {
+            update_max(mt, m_run, l_run, o);
+        }
         // Step 0 refills slot 3: every wave must be done reading K_0.
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
         barrier_no_fence();
@@ -421,12 +468,12 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 #pragma unroll
             for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
             for (; t + 1 < n_steady; t += 2) {
-                steady_step(c, t, sa, sb, o, qf, fr, m_run, l_run);
-                steady_step(c, t + 1, sb, sa, o, qf, fr, m_run, l_run);
+                steady_step<PRE>(c, t, sa, sb, o, qf, fr, m_run, l_run, negm);
+                steady_step<PRE>(c, t + 1, sb, sa, o, qf, fr, m_run, l_run, negm);
             }
         }
         for (; t < T; ++t) {
-            general_step(c, t, sa, sb, o, qf, m_run, l_run);
+            general_step<PRE>(c, t, sa, sb, o, qf, m_run, l_run, negm);
             swap_s(sa, sb);
         }
     }
@@ -488,8 +535,20 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
         }
     }
     if (lse_out && h == 0 && q < a.sq) {
-        lse_out[(int64_t)head * a.sq + q] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
+        // natural-log LSE; __builtin_amdgcn_logf is log2
+        const float lse = PRE ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2
+                              : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
+        lse_out[(int64_t)head * a.sq + q] = empty ? -INFINITY : lse;
     }
+}
+
+// One workgroup per (key split, head, 256-row query block) item, remapped so
+// each XCD works through a contiguous range of items and its concurrent
+// workgroups share one head's K/V in L2.
+template <bool PRE>
+__global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+    attend_item<PRE>(a, xcd_remap(blockIdx.x, gridDim.x), smem);
 }
 
 }  // namespace
@@ -498,7 +557,10 @@ hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     if (a.sq <= 0) return hipSuccess;
     const int nqb = (a.sq + BQ - 1) / BQ;
     const int blocks = nqb * a.num_heads * (a.n_split > 1 ? a.n_split : 1);
-    hipLaunchKernelGGL(flash_fwd_f16_d128, dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    if (a.q_log2e)
+        hipLaunchKernelGGL(flash_fwd_f16_d128<true>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(flash_fwd_f16_d128<false>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -188,16 +188,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
         barrier_no_fence();
     }
 
-    // ---- epilogue: stage the fp16 tile in LDS, then 16-byte stores
+    // ---- epilogue: stage the fp16 tile in LDS, then 16-byte stores. Pass 1
+    // (a Q tile with a q_scaled tap only) stages the Q columns again with the
+    // tap's scale and stores them to the tap.
     const bool v_tile = g.mode == kQkv && n0 >= 2 * g.hidden;
+    const int passes = (g.mode == kQkv && g.q_tap && n0 < g.hidden) ? 2 : 1;
+    for (int pass = 0; pass < passes; ++pass) {
+    if (pass == 1) __syncthreads();  // every wave is done reading pass 0's tile
     // A tile may straddle the Q|K border at column h (odd head counts), so the
     // pre-scale is chosen per column; the V border 2h is a multiple of 256.
+    const float qsc = pass == 0 ? g.q_scale : g.q_tap_scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int col = wn * 64 + j * 16 + (lane & 15);
-            const float sc = (g.mode == kQkv && n0 + col < g.hidden) ? g.q_scale : 1.0f;
+            const float sc = (g.mode == kQkv && n0 + col < g.hidden) ? qsc : 1.0f;
             const int row = wm * 128 + i * 16 + 4 * q4;
             // RMSNorm pre-norm: output row m scales by 1 / rms(x_m)
             float rsc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -237,12 +243,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f16_nt(GemmArgs g) {
                 stg16(g.c + (int64_t)m * g.ldc + n, val);
             } else {
                 const bool is_q = n < g.hidden;
+                if (pass == 1 && !is_q) continue;
                 const int nn = is_q ? n : n - g.hidden;
                 const int head = nn / g.head_dim, dd = nn % g.head_dim;
-                half_t *dst = is_q ? g.q : g.k;
+                half_t *dst = is_q ? (pass == 0 ? g.q : g.q_tap) : g.k;
                 stg16(dst + ((int64_t)head * g.M + m) * g.head_dim + dd, val);
             }
         }
+    }
     }
 }
 

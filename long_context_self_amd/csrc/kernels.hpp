@@ -51,7 +51,8 @@ struct FlashArgsF32 {
 // C[M][N] = A[M][K] * B^T with B stored [N][K] (fp16, fp32 accumulation).
 // mode kPlain: C row-major with ldc. mode kQkv: columns [0,h) are Q (scaled
 // by q_scale) -> q [H][seq][d]; [h,2h) are K -> k [H][seq][d]; [2h,3h) are V
-// -> vt [H][d][vt_ld] (transposed per head).
+// -> vt [H][d][vt_ld] (transposed per head). With q_tap set, Q is also
+// written there scaled by q_tap_scale (same layout as q).
 enum GemmMode { kPlain = 0, kQkv = 1 };
 
 struct GemmArgs {
@@ -70,6 +71,8 @@ struct GemmArgs {
     int hidden, head_dim;
     float q_scale;
     const float *row_scale;  // nullable: output row m is multiplied by row_scale[m] (RMSNorm pre-norm)
+    _Float16 *q_tap;         // nullable
+    float q_tap_scale;
 };
 
 // fp32 path: C[M][N] = A[M][K] * W[K][N] with W row-major (as given).

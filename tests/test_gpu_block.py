@@ -107,6 +107,36 @@ def test_block_f16_small_all_rows(seq, h, nh):
     _check_all_rows(seq, h, nh, np.float16, 5e-3, 2e-2)
 
 
+def test_block_every_row_every_launch():
+    """Every row of every output is written on every launch (outputs are
+    filled with NaN before each), repeated launches give the same bits, and
+    all rows match the oracle, at a size with more attention workgroups (512)
+    than CUs."""
+    seq, h, nh = 4096, 4096, 32
+    say(f"block S={seq} h={h} H={nh}, 3 launches, all rows")
+    x, [ws] = block_inputs(seq, h, 1, dtype=np.float16, seed=3)
+    blk = _block(ws, nh, seq)
+    xd = dev(x)
+    attn = torch.empty((seq, h), dtype=torch.float16, device="cuda")
+    lse = torch.empty((nh, seq), dtype=torch.float32, device="cuda")
+    y = torch.empty((seq, h), dtype=torch.float16, device="cuda")
+    outs = []
+    for _ in range(3):
+        for t in (attn, lse, y):
+            t.fill_(float("nan"))
+        blk.forward(xd, y, taps=B.Taps(None, None, None, attn.data_ptr(), lse.data_ptr(), 0))
+        torch.cuda.synchronize()
+        assert torch.isfinite(attn).all() and torch.isfinite(lse).all() and torch.isfinite(y).all()
+        outs.append((attn.clone(), lse.clone(), y.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(o, outs[0]))
+    blk.close()
+    ref = oracle.block_forward(x, *ws, nh, taps=True)
+    assert_close(host(outs[0][0]), ref["o"], what="attn_out, all rows")
+    assert_close(host(outs[0][1]), ref["lse"], what="lse, all rows")
+    assert_close(host(outs[0][2]), ref["y"], what="y, all rows")
+
+
 def test_block_f32_head_dim_128():
     _check_all_rows(200, 512, 4, np.float32, REL_L2_F32, 1e-5)
 
