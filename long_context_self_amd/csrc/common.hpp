@@ -72,8 +72,14 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
 constexpr int vmcnt_lgkm0(int n) { return (n & 0xF) | 0x70 | ((n >> 4) << 14); }
 
+// max(v of lane i, v of lane i ^ 32) in every lane. v_permlane32_swap trades
+// the upper half of one register with the lower half of the other (a VALU
+// operation, where __shfl_xor would go through the LDS crossbar); applied to
+// two copies of v it yields, in each lane i, v[i % 32] in one result and
+// v[i % 32 + 32] in the other (checked lane by lane on an MI355X).
 __device__ __forceinline__ float wave_max_across_halves(float v) {
-    return fmaxf(v, __shfl_xor(v, 32));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace attnblk

@@ -54,7 +54,7 @@ constexpr int FRAG = 64 * 8;              // halves in one MFMA operand fragment
 constexpr int NFRAG = 16;                 // fragments per K tile and per V^T tile
 constexpr int SLOT = 2 * NFRAG * FRAG;    // halves per ring slot: K part, then V^T part
 constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
-constexpr int RA = 4;                     // operand reads in flight ahead of the MFMAs
+constexpr int RA = 2;                     // operand reads in flight ahead of the MFMAs
 constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
 constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
 constexpr int OSTAGE_BYTES = NWAVES * 32 * OP32 * 4;
@@ -300,10 +300,10 @@ __device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[
         const half8 a = fr[n % RA];
         const int m = n + RA;
         fr[n % RA] = rd(m < 32 ? cur + m * FRAG : nxt + (m - 32) * FRAG);
-        // stage t+3's direct loads go out a few MFMAs into each half of the
-        // step rather than in one burst at its start
-        if (n == 4) issue_k_full(c, t + 4, t + 3);
-        if (n == 20) issue_v_full(c, t + 3, t + 3);
+        // stage t+3's direct loads go out a quarter of the way into each half
+        // of the step rather than in one burst at its start
+        if (n == 8) issue_k_full(c, t + 4, t + 3);
+        if (n == 24) issue_v_full(c, t + 3, t + 3);
         if (n < 16) {
             const int kk = n >> 1, kb = n & 1;
             sn[kb] = mfma32(a, qf[kk], kk == 0 ? (PRE ? negm : floatx16{}) : sn[kb]);
