@@ -640,7 +640,7 @@ def main() -> int:
     # CPU baseline first, in a child process, before this process touches the GPU.
     cpu = cpu_other = None
     if not args.no_cpu:
-        wl = [(seq, h, nh, 256)]
+        wl = [(seq, h, nh, 2048)]
         if not args.quick:
             wl += [(s2, 4096, 32, 256) for s2 in (8192, 16384, 32768) if s2 != seq] + [(8192, 8192, 64, 256)]
         log(f"cpu baseline: fp64 oracle, sampled rows, {len(wl)} workloads (child process)")
