@@ -395,9 +395,11 @@ attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, a
  *               stand-in for a peer's link). Host arrays of n_blocks entries.
  *   block_lens  host array, 0 <= len_b <= max_block_len (0: an empty block).
  *   o_out       device [sq][H*d] token-major in dt; lse_out NULL or fp32 [H][sq].
- * Block b is copied into slot b % 2 on the copy stream once block b-2's
- * partial has finished on `stream`, so the copy of block b+1 overlaps the
- * partial of block b; `stream` waits for each block's arrival. The copies of
+ * A block whose K and V^T are both in this device's memory is read in place.
+ * Any other block is copied into slot b % 2 on the copy stream once the
+ * partial of the block that used the slot before has finished on `stream`, so
+ * the copy of block b+1 overlaps the partial of block b; `stream` waits for
+ * each copied block's arrival. The copies of
  * a call start after the work already enqueued on `stream`; calls on one ring
  * must use one stream (or be ordered by the caller). The result equals
  * attn_partial_forward over each block followed by attn_merge_lse.

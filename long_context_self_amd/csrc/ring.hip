@@ -50,6 +50,17 @@ void free_ring(attn_ring *r) {
     delete r;
 }
 
+// True when p is device memory of `device` (ordinary or managed allocations
+// report other types and are copied).
+bool on_device(const void *p, int device) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // e.g. unregistered host memory: not device memory
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice && attr.device == device;
+}
+
 }  // namespace
 
 ATTN_API attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, attn_dtype_t dt,
@@ -131,22 +142,32 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
         const int slot = b & 1;
         const int64_t len = block_lens[b];
         const int64_t ld = ATTN_VT_LD(len);
-        if (b >= 2) HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(ring->copy, ring->freed[slot], 0));
-        if (len > 0) {
-            HIP_TRY("attn_ring_forward: K copy", hipMemcpyAsync(ring->slot_k[slot], k_blocks[b], (size_t)H * len * d * es,
-                                                                hipMemcpyDefault, ring->copy));
-            HIP_TRY("attn_ring_forward: V copy", hipMemcpyAsync(ring->slot_vt[slot], vt_blocks[b],
-                                                                (size_t)H * d * ld * es, hipMemcpyDefault, ring->copy));
+        // A block already in this device's memory is read where it is; any other
+        // block (pinned host memory, a peer's memory) is copied into a slot.
+        const bool in_place = len > 0 && on_device(k_blocks[b], ring->device) && on_device(vt_blocks[b], ring->device);
+        const void *kb = in_place ? k_blocks[b] : ring->slot_k[slot];
+        const void *vb = in_place ? vt_blocks[b] : ring->slot_vt[slot];
+        if (!in_place) {
+            if (b >= 2)
+                HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(ring->copy, ring->freed[slot], 0));
+            if (len > 0) {
+                HIP_TRY("attn_ring_forward: K copy", hipMemcpyAsync(ring->slot_k[slot], k_blocks[b],
+                                                                    (size_t)H * len * d * es, hipMemcpyDefault,
+                                                                    ring->copy));
+                HIP_TRY("attn_ring_forward: V copy", hipMemcpyAsync(ring->slot_vt[slot], vt_blocks[b],
+                                                                    (size_t)H * d * ld * es, hipMemcpyDefault,
+                                                                    ring->copy));
+            }
+            HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->arrived[slot], ring->copy));
+            HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(stream, ring->arrived[slot], 0));
         }
-        HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->arrived[slot], ring->copy));
-        HIP_TRY("attn_ring_forward: hipStreamWaitEvent", hipStreamWaitEvent(stream, ring->arrived[slot], 0));
         float *ob = ring->o_parts + (size_t)b * H * sq * d;
         float *lb = ring->lse_parts + (size_t)b * H * sq;
         if (ring->dt == kF16) {
             FlashArgs fa{};
             fa.q = static_cast<const _Float16 *>(q_scaled);
-            fa.k = static_cast<const _Float16 *>(ring->slot_k[slot]);
-            fa.vt = static_cast<const _Float16 *>(ring->slot_vt[slot]);
+            fa.k = static_cast<const _Float16 *>(kb);
+            fa.vt = static_cast<const _Float16 *>(vb);
             fa.q_head_stride = sq * d;
             fa.k_head_stride = len * d;
             fa.v_head_stride = (int64_t)d * ld;
@@ -160,8 +181,8 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
         } else {
             FlashArgsF32 fa{};
             fa.q = static_cast<const float *>(q_scaled);
-            fa.k = static_cast<const float *>(ring->slot_k[slot]);
-            fa.vt = static_cast<const float *>(ring->slot_vt[slot]);
+            fa.k = static_cast<const float *>(kb);
+            fa.vt = static_cast<const float *>(vb);
             fa.q_head_stride = sq * d;
             fa.k_head_stride = len * d;
             fa.v_head_stride = (int64_t)d * ld;
