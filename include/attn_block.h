@@ -232,7 +232,11 @@ attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int6
  * `stream` and released on it after the kernels; the pool keeps the memory
  * for reuse). That pass reads and writes H*skv*d elements more than
  * attn_partial_forward_vt, which takes V^T directly. Calls on different
- * streams may overlap.
+ * streams may overlap. In fp16, a call whose grid would leave a last round
+ * of workgroups partly idle runs the last query rows of each head split over
+ * key ranges and merges them by LSE (the same plan for the same num_heads, sq
+ * and skv, in every partial entry point and in attn_ring_forward); those
+ * partials, at most 64 MiB, come from the same pool.
  * Pointers 16-byte aligned; head strides multiples of 8 (ATTN_F16) or 4
  * (ATTN_F32), q_head_stride >= sq*d and kv_head_stride >= skv*d when
  * num_heads > 1. sq = 0 enqueues nothing. skv = 0 writes o_part = 0 and
@@ -248,14 +252,14 @@ attn_status_t attn_partial_forward(int num_heads, int head_dim, attn_dtype_t dt,
 /*
  * attn_partial_forward_vt -- attn_partial_forward with V given transposed per
  * head (keys contiguous), the layout the block's projection writes (the v_t
- * tap) and the attention kernel reads, so no staging pass and no allocation.
+ * tap) and the attention kernel reads, so no staging pass.
  * [Same definition and sources as attn_partial_forward.]
  *   k         element (j,t,c) at k[j*k_head_stride + t*head_dim + c], t < skv.
  *   v_t       element (j,c,t) at v_t[j*v_head_stride + c*v_row_stride + t]
  *             (V transposed per head: keys contiguous).
- * Other arguments, outputs and errors as for attn_partial_forward (no
- * ATTN_E_OOM). v_row_stride >= skv and a multiple of 8 (ATTN_F16) or 4
- * (ATTN_F32).
+ * Other arguments, outputs and errors as for attn_partial_forward
+ * (ATTN_E_OOM only from the split partials of the fp16 plan). v_row_stride >=
+ * skv and a multiple of 8 (ATTN_F16) or 4 (ATTN_F32).
  */
 attn_status_t attn_partial_forward_vt(int num_heads, int head_dim, attn_dtype_t dt,
                                       const void *q_scaled, int64_t sq, int64_t q_head_stride,
@@ -266,9 +270,10 @@ attn_status_t attn_partial_forward_vt(int num_heads, int head_dim, attn_dtype_t 
 /*
  * attn_partial_forward_noalloc -- attn_partial_forward for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
- * loops, harnesses that forbid allocation): the V^T staging lives in a fixed
- * 64 MiB device array of the library instead of the stream-ordered pool, and
- * the call makes no allocation of any kind.
+ * loops, harnesses that forbid allocation): the V^T staging (up to 64 MiB)
+ * and the split partials of the fp16 plan (up to 64.5 MiB) live in a fixed
+ * 128.5 MiB device array of the library instead of the stream-ordered pool,
+ * and the call makes no allocation of any kind.
  *   Arguments, layouts and results: as attn_partial_forward (bit-identical
  *   output).
  *   Limit: num_heads * head_dim * ATTN_VT_LD(skv) * element size <= 64 MiB
@@ -302,7 +307,12 @@ attn_status_t attn_partial_forward_noalloc(int num_heads, int head_dim, attn_dty
  *                or 4 (fp32);
  *   lse          NULL or fp32 [H][seq], natural-log.
  * head_dim 128 (ATTN_F16) or 64/128 (ATTN_F32); pointers 16-byte aligned.
- * seq = 0 enqueues nothing.
+ * seq = 0 enqueues nothing. In fp16, when the grid would leave a last round
+ * of workgroups partly idle, the last query rows of each head run split over
+ * key ranges and are merged by LSE; those partials (at most 256 MiB) come from
+ * the library's stream-ordered pool, allocated and released on `stream`.
+ * Errors: ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_OOM (the split
+ * partials), ATTN_E_HIP.
  */
 attn_status_t attn_heads_forward(int num_heads, int head_dim, attn_dtype_t dt, const void *q_scaled,
                                  const void *k, const void *v_t, int64_t seq, void *o, int64_t o_ld,

@@ -12,24 +12,28 @@
 // that block's normalised partial and its LSE.
 //
 // Design (MI355X):
-// * One workgroup = 256 query rows of one head, 8 waves (2 per SIMD), 32 rows
-//   per wave; K and V^T tiles of 64 keys.
-// * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_f16, Q held in
-//   registers as the B operand of S. K rows are taken in a permuted order so
-//   that each lane's S accumulator holds 16 consecutive keys of its own query;
-//   after exp and a cast those are the B operand of the PV product, with no
-//   data movement between lanes.
-// * Software pipeline per wave: step t issues the MFMAs of S_{t+1} and of
-//   O += V_t P_t, and while they run computes exp(S_t) -> P_t (before the PV
-//   MFMAs that need it) and then the row sums of P_t and the row maxima of
-//   S_{t+1}. The VALU softmax work thus hides under the wave's own matrix work
-//   instead of alternating with it.
+// * One workgroup = 384 query rows of one head, 8 waves (2 per SIMD), 48 rows
+//   per wave as three 16-row blocks; K and V^T stages of 64 keys, worked in
+//   two 32-key halves.
+// * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16, Q held in
+//   registers as the B operand of S. Every K or V^T fragment read from LDS
+//   feeds three MFMAs (one per query block), so a wave moves two thirds of
+//   the LDS operand bytes per product that a 32-row wave would, and each K/V
+//   stage brought into LDS serves 384 rows.
+// * K rows are taken in a permuted order so that each lane's S accumulators
+//   hold 8 consecutive keys of its own query; after exp and a cast those are
+//   the B operand of the PV product, with no data movement between lanes.
+// * Software pipeline per wave: each half-step issues the MFMAs of the next
+//   32 keys' scores and of O += V P for the current 32 keys, and computes
+//   exp(S) -> P before the PV MFMAs that need it, then the row sums of P and
+//   the row maxima of the next scores, so the softmax VALU work shares the
+//   wave's instruction stream with its own matrix work.
 // * K/V^T reach LDS by direct global->LDS loads (no staging registers) into a
-//   4-slot ring, issued three steps ahead. LDS holds every tile in MFMA
-//   operand order: fragment n of a tile is 64 lanes x 16 bytes, so every
+//   4-slot ring, issued three stages ahead. LDS holds every tile in MFMA
+//   operand order: fragment n of a stage is 64 lanes x 16 bytes, so every
 //   operand read is one lane-linear ds_read_b128 (conflict-free, base register
 //   plus immediate), and each load instruction gathers exactly one fragment.
-//   One barrier per step; the next step's first operands are read before it.
+//   One barrier per stage; the next stage's first operands are read before it.
 // * Softmax in the exp2 domain with the running max and sum in registers; the
 //   O rescale is skipped unless some row's max grew by more than 2^8 (exact:
 //   O and the sum always share the same reference max).
@@ -37,6 +41,9 @@
 //   16-byte chunks of whole lines.
 // * Blocks are remapped so each XCD works through a contiguous range of
 //   (head, query block) items and its concurrent workgroups share K/V in L2.
+
+#include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -46,47 +53,61 @@ namespace attnblk {
 namespace {
 
 constexpr int D = 128;       // head_dim
-constexpr int BQ = 256;      // query rows per workgroup
+constexpr int NQ = 3;        // 16-row query blocks per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int BN = 64;       // keys per tile
-constexpr int FRAG = 64 * 8;              // halves in one MFMA operand fragment
-constexpr int NFRAG = 16;                 // fragments per K tile and per V^T tile
-constexpr int SLOT = 2 * NFRAG * FRAG;    // halves per ring slot: K part, then V^T part
+constexpr int BQ = NWAVES * 16 * NQ;  // query rows per workgroup (384)
+constexpr int BN = 64;                // keys per stage
+constexpr int FRAG = 64 * 8;          // halves in one MFMA operand fragment
+constexpr int HFRAG = 16;             // fragments per half-stage: 8 of K, then 8 of V^T
+constexpr int SLOT = 2 * HFRAG * FRAG;    // halves per ring slot
 constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
 constexpr int RA = 2;                     // operand reads in flight ahead of the MFMAs
 constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
 constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
-constexpr int OSTAGE_BYTES = NWAVES * 32 * OP32 * 4;
-constexpr int SMEM_BYTES = RING_BYTES > OSTAGE_BYTES ? RING_BYTES : OSTAGE_BYTES;
+constexpr int OSTAGE16 = NWAVES * 16 * NQ * OP16 * 2;
+constexpr int OSTAGE32 = NWAVES * 16 * OP32 * 4;
+constexpr int SMEM_BYTES = RING_BYTES;
+static_assert(OSTAGE16 <= RING_BYTES && OSTAGE32 <= RING_BYTES, "O staging reuses the ring");
 constexpr float kRescaleTau = 8.0f * kLn2;  // rescale only when a max grows by > 2^8
 
-// Accumulator row i of a 32x32 S^T block holds key perm_key(i) of its 32-key
-// block: lane half h then owns keys 16h..16h+15 in accumulator order.
-__device__ __forceinline__ int perm_key(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+// v_mfma_f32_16x16x32_f16: C[16x16] += A[16x32] * B[32x16]. Lane l supplies A
+// row (l % 16), k = 8*(l/16) + j, j < 8, and B column (l % 16) with the same
+// k; accumulator element r of lane l is C[4*(l/16) + r][l % 16].
+__device__ __forceinline__ floatx4 mfma16(const half8 &a, const half8 &b, const floatx4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
-// Stage s = {K_{s+1}, V_s}: everything step s reads. Fragment order:
-// * K fragment n (MFMA n of a step): k-step kk = n / 2 (head dims 16kk..),
-//   key block kb = n % 2. Lane l holds K[32kb + perm_key(l % 32)][16kk + 8(l / 32) + 0..7].
-// * V^T fragment n (MFMA 16 + n): head-dim block mb = n % 4, key step ks = n / 4
-//   (key block ks / 2, half ks % 2). Lane l holds
-//   V^T[32mb + l % 32][32(ks / 2) + 16(l / 32) + 8(ks % 2) + 0..7], matching the
-//   key order of the lane's P values.
-// Wave w moves K and V^T fragments 2w and 2w + 1 of every stage.
+__device__ __forceinline__ floatx4 splat4(float v) { return floatx4{v, v, v, v}; }
+
+// Row m of the 16-row S^T block kb (0 or 1) of a 32-key half holds key
+// kperm(kb, m) of that half, so that accumulator element r of lane l holds key
+// 8*(l/16) + 4*kb + r: the lane's two blocks together hold keys
+// 8*(l/16)..8*(l/16)+7 of its query, in order.
+__device__ __forceinline__ int kperm(int kb, int m) { return 8 * (m >> 2) + 4 * kb + (m & 3); }
+
+// Stage s: half u (0, 1) holds K of key half 2s+1+u and V^T of key half 2s+u
+// (32 keys each), so step s reads only stage s. Fragment order within half u:
+// * K fragment n < 8 (head-dim step kk = n / 2, key block kb = n % 2): lane l
+//   holds K[kperm(kb, l % 16)][32kk + 8(l / 16) + 0..7] of its key half.
+// * V^T fragment 8 + mb (head-dim block mb < 8): lane l holds
+//   V^T[16mb + l % 16][8(l / 16) + 0..7] of its key half.
+// Wave w moves K fragments 2w, 2w + 1 and V^T fragments 2w, 2w + 1 of the 16
+// of each kind in a stage (index 8u + n), so waves 0-3 fill half 0.
 struct LoadOffsets {
-    uint32_t k[2], v[2];  // bytes from the tile's first key
+    uint32_t k[2], v[2];  // bytes from the stage's first key of that kind
 };
 
 __device__ __forceinline__ LoadOffsets load_offsets(const FlashArgs &a, int wave, int lane) {
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane & 15, g = lane >> 4;
     LoadOffsets o;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int n = 2 * wave + e;
+        const int f = 2 * wave + e;  // 0..15
+        const int u = f >> 3, n = f & 7;
         const int kk = n >> 1, kb = n & 1;
-        o.k[e] = (uint32_t)(((kb * 32 + perm_key(r)) * D + kk * 16 + 8 * h) * 2);
-        const int mb = n & 3, ks = n >> 2;
-        o.v[e] = (uint32_t)(((int64_t)(32 * mb + r) * a.v_row_stride + 32 * (ks >> 1) + 16 * h + 8 * (ks & 1)) * 2);
+        o.k[e] = (uint32_t)(((32 * u + kperm(kb, r)) * D + 32 * kk + 8 * g) * 2);
+        o.v[e] = (uint32_t)(((int64_t)(16 * n + r) * a.v_row_stride + 32 * u + 8 * g) * 2);
     }
     return o;
 }
@@ -96,12 +117,17 @@ struct Ctx {
     char *ring;           // LDS ring (wave-uniform)
     const half_t *rl;     // LDS ring + 8 * lane (this lane's operand slot)
     LoadOffsets lo;
-    int wave, lane, skv, T;
+    int wave, lane, skv, NH, T;  // NH: 32-key halves, T: stages
     int64_t vrs;
 };
 
-__device__ __forceinline__ char *slot_k(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2; }
-__device__ __forceinline__ char *slot_v(const Ctx &c, int s) { return c.ring + (s & 3) * SLOT * 2 + NFRAG * FRAG * 2; }
+// LDS byte address of the e-th fragment of kind K (0) or V^T (1) that this
+// wave loads, in the slot of stage s.
+__device__ __forceinline__ char *frag_dst(const Ctx &c, int s, int kind, int e) {
+    const int f = 2 * c.wave + e;
+    const int u = f >> 3, n = f & 7;
+    return c.ring + ((s & 3) * SLOT + (u * HFRAG + kind * 8 + n) * FRAG) * 2;
+}
 
 // Buffer descriptor for raw byte addressing from `base` (stride 0, no
 // range clamp): the tile base lives in scalar registers and each lane adds
@@ -110,286 +136,306 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, -1, 0x00020000);
 }
 
-// Full K tile `tile` -> K part of slot s (two direct loads per wave).
-__device__ __forceinline__ void issue_k_full(const Ctx &c, int tile, int s) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.kh + (int64_t)tile * BN * D * 2);
-    char *dst = slot_k(c, s) + 2 * c.wave * FRAG * 2;
+// K of stage s >= 0 (keys 64s + 32 .. 64s + 96, all present) -> slot s.
+__device__ __forceinline__ void issue_k_full(const Ctx &c, int s) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.kh + ((int64_t)s * BN + 32) * D * 2);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + e * FRAG * 2), 16, c.lo.k[e], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)frag_dst(c, s, 0, e), 16, c.lo.k[e], 0, 0, 0);
 }
 
-// Full V^T tile -> V part of slot s.
-__device__ __forceinline__ void issue_v_full(const Ctx &c, int tile, int s) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.vh + (int64_t)tile * BN * 2);
-    char *dst = slot_v(c, s) + 2 * c.wave * FRAG * 2;
+// V^T of stage s >= 0 (keys 64s .. 64s + 64, all present) -> slot s.
+__device__ __forceinline__ void issue_v_full(const Ctx &c, int s) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.vh + (int64_t)s * BN * 2);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + e * FRAG * 2), 16, c.lo.v[e], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)frag_dst(c, s, 1, e), 16, c.lo.v[e], 0, 0, 0);
 }
 
-// Last, partial K tile: rows past skv are clamped to the last key (finite
-// values; their scores are masked).
-__device__ __forceinline__ void issue_k_partial(const Ctx &c, int tile, int s) {
-    const int r = c.lane & 31, h = c.lane >> 5;
-    char *dst = slot_k(c, s) + 2 * c.wave * FRAG * 2;
+// This wave's K fragments of stage s when a key half of it is partial or
+// missing: halves outside [0, NH) are skipped, rows past skv are clamped to
+// the last key (finite values; their scores are masked). Returns the number
+// of direct loads issued.
+__device__ __forceinline__ int issue_k_partial(const Ctx &c, int s) {
+    const int r = c.lane & 15, g = c.lane >> 4;
+    int n_issued = 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int n = 2 * c.wave + e;
+        const int f = 2 * c.wave + e;
+        const int u = f >> 3, n = f & 7;
         const int kk = n >> 1, kb = n & 1;
-        const int key = min(tile * BN + kb * 32 + perm_key(r), c.skv - 1);
-        const char *src = c.kh + ((int64_t)key * D + kk * 16 + 8 * h) * 2;
-        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + e * FRAG * 2), 16, 0, 0);
+        const int half = 2 * s + 1 + u;
+        if (half < 0 || half >= c.NH) continue;  // wave-uniform
+        const int key = min(32 * half + kperm(kb, r), c.skv - 1);
+        const char *src = c.kh + ((int64_t)key * D + 32 * kk + 8 * g) * 2;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)frag_dst(c, s, 0, e), 16, 0, 0);
+        ++n_issued;
     }
+    return n_issued;
 }
 
-// Last, partial V^T tile through registers: keys past skv are stored as
-// zeros, so the zero probabilities of masked keys never meet non-finite data.
-__device__ __forceinline__ void stage_v_partial(const Ctx &c, int tile, int s) {
-    const int r = c.lane & 31, h = c.lane >> 5;
-    half_t *dst = reinterpret_cast<half_t *>(slot_v(c, s)) + 2 * c.wave * FRAG + 8 * c.lane;
+// This wave's V^T fragments of stage s through registers: keys past skv are
+// stored as zeros, so the zero probabilities of masked keys never meet
+// non-finite data.
+__device__ __forceinline__ void stage_v_partial(const Ctx &c, int s) {
+    const int r = c.lane & 15, g = c.lane >> 4;
     const half_t *vh = reinterpret_cast<const half_t *>(c.vh);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int n = 2 * c.wave + e;
-        const int mb = n & 3, ks = n >> 2;
-        const int key = tile * BN + 32 * (ks >> 1) + 16 * h + 8 * (ks & 1);
-        const half_t *src = vh + (int64_t)(32 * mb + r) * c.vrs + key;
+        const int f = 2 * c.wave + e;
+        const int u = f >> 3, mb = f & 7;
+        const int half = 2 * s + u;
+        if (half < 0 || half >= c.NH) continue;  // wave-uniform
+        const int key = 32 * half + 8 * g;
+        const half_t *src = vh + (int64_t)(16 * mb + r) * c.vrs + key;
         half8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (key + j < c.skv) ? src[j] : (half_t)0.0f;
-        *reinterpret_cast<half8 *>(dst + e * FRAG) = v;
+        *reinterpret_cast<half8 *>(frag_dst(c, s, 1, e) + 16 * c.lane) = v;
     }
 }
 
 // Issue stage s (any position in the key loop); returns the number of direct
-// loads it left in flight (register-path loads complete before returning).
+// loads it left in flight (register-path stores complete before returning).
 __device__ __forceinline__ int issue_stage(const Ctx &c, int s) {
     int n = 0;
-    const int kt = s + 1;
-    if (kt < c.T) {
-        if ((kt + 1) * BN <= c.skv)
-            issue_k_full(c, kt, s);
-        else
-            issue_k_partial(c, kt, s);
-        n += 2;
-    }
-    if (s >= 0 && s < c.T) {
-        if ((s + 1) * BN <= c.skv) {
-            issue_v_full(c, s, s);
+    if (2 * s + 1 < c.NH) {  // some K half of the stage exists
+        if (s >= 0 && (int64_t)s * BN + 96 <= c.skv) {
+            issue_k_full(c, s);
             n += 2;
         } else {
-            stage_v_partial(c, s, s);
+            n += issue_k_partial(c, s);
+        }
+    }
+    if (s >= 0 && 2 * s < c.NH) {  // some V^T half of the stage exists
+        if ((int64_t)(s + 1) * BN <= c.skv) {
+            issue_v_full(c, s);
+            n += 2;
+        } else {
+            stage_v_partial(c, s);
         }
     }
     return n;
 }
 
-// Wait until at most n direct loads are in flight and every LDS access of
-// this wave is complete.
+// Wait until at most n (<= 4) direct loads are in flight and every LDS access
+// of this wave is complete.
 __device__ __forceinline__ void wait_vm_lgkm(int n) {
     if (n >= 4)
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(4));
-    else if (n >= 2)
+    else if (n == 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(3));
+    else if (n == 2)
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(2));
+    else if (n == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(1));
     else
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
 }
 
 __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<const half8 *>(p); }
 
+typedef floatx4 SBlk[2][NQ];  // scores of one 32-key half: [key block][query block]
+
 // P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
-// pf[ks] holds keys 32(ks / 2) + 16h + 8(ks % 2) + 0..7 of the lane's query.
+// pf[j] holds keys 8(l / 16) + 0..7 of the lane's query in block j.
 // PRE: the scores are already (S - m) log2(e) -- Q carries the log2(e)
 // factor and the first S MFMA starts from -m (see the kernel) -- so P is one
 // exp2 per score; otherwise one FMA per score maps S to that argument.
 template <bool PRE>
-__device__ __forceinline__ void exp_and_pack(const floatx16 (&sc)[2], half8 (&pf)[4], float mneg) {
+__device__ __forceinline__ void exp_and_pack(const SBlk &sc, half8 (&pf)[NQ], const float (&m_run)[NQ]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < NQ; ++j) {
+        const float mneg = -m_run[j] * kLog2e;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            pf[2 * kb + (i >> 3)][i & 7] =
-                (half_t)__builtin_amdgcn_exp2f(PRE ? sc[kb][i] : fmaf(sc[kb][i], kLog2e, mneg));
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pf[j][4 * kb + r] =
+                    (half_t)__builtin_amdgcn_exp2f(PRE ? sc[kb][j][r] : fmaf(sc[kb][j][r], kLog2e, mneg));
+    }
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-// Row sum of the fp16 probabilities (the very values the PV product
-// weights), two per dot instruction with fp32 accumulation.
-__device__ __forceinline__ float row_sum(const half8 (&pf)[4]) {
+// Add the fp16 probabilities (the very values the PV product weights) to the
+// lane's running sums, two per dot instruction with fp32 accumulation.
+__device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_run)[NQ]) {
     const half2v one = {(half_t)1.0f, (half_t)1.0f};
-    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int j = 0; j < NQ; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-            a0 = __builtin_amdgcn_fdot2(half2v{pf[ks][2 * j], pf[ks][2 * j + 1]}, one, a0, false);
-            a1 = __builtin_amdgcn_fdot2(half2v{pf[ks][2 * j + 2], pf[ks][2 * j + 3]}, one, a1, false);
-        }
-    return a0 + a1;
+        for (int i = 0; i < 8; i += 2)
+            l_run[j] = __builtin_amdgcn_fdot2(half2v{pf[j][i], pf[j][i + 1]}, one, l_run[j], false);
 }
 
+// max(v) over lanes i, i ^ 16, i ^ 32, i ^ 48 (the four lanes that hold one
+// query's keys). v_permlane16_swap trades the odd 16-lane rows of one
+// register with the even rows of the other; applied to two copies of v it
+// yields v of lane i and of lane i ^ 16 in every lane i.
+__device__ __forceinline__ float max_over_key_lanes(float v) {
+    v = wave_max_across_halves(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Each lane's maximum over its own 8 scores of every query block, for key
+// half `half`, masking keys past skv. The row maximum is that over the four
+// lanes of the query (max_over_key_lanes).
 template <bool MASK>
-__device__ __forceinline__ float row_max(floatx16 (&s)[2], int key0, int skv, int h) {
+__device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, float (&lm)[NQ]) {
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (key0 + 32 * kb + 16 * h + i >= skv) s[kb][i] = -INFINITY;
-    }
-    // two chains of three-operand maxima over the 32 scores
-    float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
+            for (int r = 0; r < 4; ++r) {
+                const bool out = 32 * half + 8 * g + 4 * kb + r >= skv;
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-        m0 = fmaxf(fmaxf(m0, s[0][i]), s[0][i + 1]);
-        m1 = fmaxf(fmaxf(m1, s[1][i]), s[1][i + 1]);
+                for (int j = 0; j < NQ; ++j)
+                    if (out) s[kb][j][r] = -INFINITY;
+            }
     }
-    return wave_max_across_halves(fmaxf(m0, m1));
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        // three-operand max chains: four instructions for eight values
+        const float a = fmaxf(fmaxf(s[0][j][0], s[0][j][1]), s[0][j][2]);
+        const float b = fmaxf(fmaxf(s[0][j][3], s[1][j][0]), s[1][j][1]);
+        lm[j] = fmaxf(fmaxf(fmaxf(a, b), s[1][j][2]), s[1][j][3]);
+    }
 }
 
-// New row max mt of the next scores: raise the reference max where it grew by
-// more than 2^8 and rescale O and the running sum to it (skipped when no row
-// of the wave needs it).
-__device__ __forceinline__ void update_max(float mt, float &m_run, float &l_run, floatx16 (&o)[4]) {
-    const bool need = mt > m_run + kRescaleTau;
-    if (__ballot(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-        m_run = m_new;
-        l_run *= alpha;
+// Given the lanes' local maxima lm of the next scores: where some row's max
+// grew by more than 2^8, raise its reference to the new row max and rescale O
+// and the running sum to it. A lane whose own scores stay within 2^8 of the
+// reference says nothing about the rest of its row, so the row maxima (a
+// reduction over four lanes) are formed only when some lane of the wave is
+// over; otherwise every score of the wave is within 2^8 and nothing changes.
+__device__ __forceinline__ void update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+                                           floatx4 (&o)[8][NQ]) {
+    bool over = false;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
+    for (int j = 0; j < NQ; ++j) over = over || lm[j] > m_run[j] + kRescaleTau;
+    if (__ballot(over)) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const float mt = max_over_key_lanes(lm[j]);
+            const float m_new = mt > m_run[j] + kRescaleTau ? mt : m_run[j];
+            const float alpha = __builtin_amdgcn_exp2f((m_run[j] - m_new) * kLog2e);
+            m_run[j] = m_new;
+            l_run[j] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
+        }
     }
 }
 
 // The same for PRE scores, which are relative to the reference already
-// (log2 units): mt is the row max of S - m. Where it exceeds 8 the reference
-// moves up by mt, and O, the sum, the pending scores and the accumulator
-// start value -m of later tiles follow it.
-__device__ __forceinline__ void update_max_rel(float mt, float &m_run, float &l_run, floatx16 (&o)[4],
-                                               floatx16 (&s)[2], floatx16 &negm) {
-    const bool need = mt > 8.0f;
-    if (__ballot(need)) {
-        const float delta = need ? mt : 0.0f;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        m_run += delta;
-        l_run *= alpha;
+// (log2 units): the row max mt of S - m. Where it exceeds 8 the reference
+// moves up by mt, and O, the sum and the pending scores follow it (later
+// halves start their S accumulators from the new -m).
+__device__ __forceinline__ void update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+                                               floatx4 (&o)[8][NQ], SBlk &s) {
+    bool over = false;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
+    for (int j = 0; j < NQ; ++j) over = over || lm[j] > 8.0f;
+    if (__ballot(over)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
-        negm = -m_run;
+        for (int j = 0; j < NQ; ++j) {
+            const float mt = max_over_key_lanes(lm[j]);
+            const float delta = mt > 8.0f ? mt : 0.0f;
+            const float alpha = __builtin_amdgcn_exp2f(-delta);
+            m_run[j] += delta;
+            l_run[j] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb][j] -= delta;
+        }
     }
 }
 
-// Steady step t: every tile it touches is full, stage t+3 exists and is
-// full, and step t+1 starts with S_{t+2} MFMAs. fr holds this step's first
-// RA operands on entry and the next step's on exit.
-template <bool PRE>
-__device__ __forceinline__ void steady_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
-                                            floatx16 (&o)[4], const half8 (&qf)[8], half8 (&fr)[RA],
-                                            float &m_run, float &l_run, floatx16 &negm) {
+struct State {
+    floatx4 o[8][NQ];  // O^T accumulators [head-dim block][query block]
+    half8 qf[NQ][4];   // Q as B operands [query block][head-dim step]
+    float m_run[NQ], l_run[NQ];
+};
+
+// Half U of step t: P of key half 2t+U from sc, O += V P over it, and the
+// scores of key half 2t+U+1 into sn (their row maxima folded into the
+// reference). STEADY: every half this step touches and stage t+3 are full;
+// fr holds the next RA operands on entry and exit, running on into the next
+// stage, and stage t+3's direct loads go out at fixed points. Otherwise every
+// condition is checked and reads stay within the half.
+template <bool PRE, bool STEADY, int U>
+__device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &sn, State &st, half8 (&fr)[RA]) {
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
-    half8 pf[4];
-    exp_and_pack<PRE>(sc, pf, -m_run * kLog2e);
+    const int hv = 2 * t + U;  // key half of this PV
+    const bool has_pv = STEADY || hv < c.NH;
+    const bool has_s = STEADY || hv + 1 < c.NH;
+    half8 pf[NQ];
+    if (has_pv) exp_and_pack<PRE>(sc, pf, st.m_run);
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-        const half8 a = fr[n % RA];
-        const int m = n + RA;
-        fr[n % RA] = rd(m < 32 ? cur + m * FRAG : nxt + (m - 32) * FRAG);
-        // stage t+3's direct loads go out a quarter of the way into each half
-        // of the step rather than in one burst at its start
-        if (n == 8) issue_k_full(c, t + 4, t + 3);
-        if (n == 24) issue_v_full(c, t + 3, t + 3);
-        if (n < 16) {
-            const int kk = n >> 1, kb = n & 1;
-            sn[kb] = mfma32(a, qf[kk], kk == 0 ? (PRE ? negm : floatx16{}) : sn[kb]);
+    for (int n = 0; n < HFRAG; ++n) {
+        if (!(n < 8 ? has_s : has_pv)) continue;  // wave-uniform
+        half8 a;
+        if (STEADY) {
+            a = fr[n % RA];
+            const int m = U * HFRAG + n + RA;
+            fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
+            // stage t+3's direct loads go out a quarter of the way into each
+            // half-step rather than in one burst at the step's start
+            if (U == 0 && n == 4) issue_k_full(c, t + 3);
+            if (U == 1 && n == 4) issue_v_full(c, t + 3);
         } else {
-            const int mb = (n - 16) & 3, ks = (n - 16) >> 2;
-            o[mb] = mfma32(a, pf[ks], o[mb]);
+            a = rd(cur + (U * HFRAG + n) * FRAG);
         }
-    }
-    l_run += row_sum(pf);
-    if (PRE)
-        update_max_rel(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o, sn, negm);
-    else
-        update_max(row_max<false>(sn, 0, 0, c.lane >> 5), m_run, l_run, o);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
-    barrier_no_fence();
-}
-
-// Any step t (the last few of the loop): the same work with every condition
-// checked, and without reading ahead into the next step.
-template <bool PRE>
-__device__ __forceinline__ void general_step(const Ctx &c, int t, floatx16 (&sc)[2], floatx16 (&sn)[2],
-                                             floatx16 (&o)[4], const half8 (&qf)[8], float &m_run,
-                                             float &l_run, floatx16 &negm) {
-    const int inflight = issue_stage(c, t + 3);
-    const half_t *cur = c.rl + (t & 3) * SLOT;
-    half8 pf[4];
-    exp_and_pack<PRE>(sc, pf, -m_run * kLog2e);
-    const bool has_s = t + 1 < c.T;
-    if (has_s) {
-        half8 fa[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) fa[n] = rd(cur + n * FRAG);
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        if (n < 8) {
             const int kk = n >> 1, kb = n & 1;
-            sn[kb] = mfma32(fa[n], qf[kk], kk == 0 ? (PRE ? negm : floatx16{}) : sn[kb]);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                sn[kb][j] = mfma16(a, st.qf[j][kk], kk == 0 ? (PRE ? splat4(-st.m_run[j]) : floatx4{}) : sn[kb][j]);
+        } else {
+            const int mb = n - 8;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) st.o[mb][j] = mfma16(a, pf[j], st.o[mb][j]);
         }
     }
-    {
-        half8 fb[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) fb[n] = rd(cur + (NFRAG + n) * FRAG);
-#pragma unroll
-        for (int n = 0; n < 16; ++n) o[n & 3] = mfma32(fb[n], pf[n >> 2], o[n & 3]);
-    }
-    l_run += row_sum(pf);
+    if (has_pv) add_row_sums(pf, st.l_run);
     if (has_s) {
-        const int key0 = (t + 1) * BN;
-        const float mt = (key0 + BN <= c.skv) ? row_max<false>(sn, key0, c.skv, c.lane >> 5)
-                                               : row_max<true>(sn, key0, c.skv, c.lane >> 5);
-        if (PRE)
-            update_max_rel(mt, m_run, l_run, o, sn, negm);
+        float lm[NQ];
+        const int g = c.lane >> 4;
+        if (STEADY || 32 * (hv + 2) <= c.skv)
+            local_max<false>(sn, hv + 1, c.skv, g, lm);
         else
-            update_max(mt, m_run, l_run, o);
-        wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
-        barrier_no_fence();
+            local_max<true>(sn, hv + 1, c.skv, g, lm);
+        if (PRE)
+            update_max_rel(lm, st.m_run, st.l_run, st.o, sn);
+        else
+            update_max(lm, st.m_run, st.l_run, st.o);
     }
 }
 
-__device__ __forceinline__ void swap_s(floatx16 (&a)[2], floatx16 (&b)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const floatx16 t = a[kb];
-        a[kb] = b[kb];
-        b[kb] = t;
-    }
-}
-
-// Stage s holds K_{s+1} and V_s; the prologue loads K_0 as stage -1 (slot 3)
-// and stages 0..2, computes S_0 and its row max. Step t (0 <= t < T) adds
-// V_t P_t into O and computes S_{t+1}; it issues stage t+3 into the slot that
-// stage t-1 used (all of whose reads finished before the barrier that ended
-// step t-1) and ends by waiting for stage t+2 and a barrier, so step t+1 may
-// read stage t+1's operands ahead of that barrier.
+// Stage s holds K of key halves 2s+1, 2s+2 and V^T of halves 2s, 2s+1; the
+// prologue loads K of half 0 as stage -1 (slot 3) and stages 0..2, and
+// computes S of half 0 and its row max. Step t (0 <= t < T) adds V P of
+// halves 2t, 2t+1 into O and computes S of halves 2t+1, 2t+2; it issues stage
+// t+3 into the slot that stage t-1 used (all of whose reads finished before
+// the barrier that ended step t-1) and ends by waiting for stage t+2 and a
+// barrier, so step t+1 may read stage t+1's operands ahead of that barrier.
 //
 // PRE (set when q holds q_scaled * log2(e), as the block's projection writes
 // it): the scores come out of the S MFMAs already as (S - m) log2(e) -- the
 // log2(e) factor rides in Q and the first MFMA of each S chain starts from
-// the accumulator value -m (negm) instead of 0 -- so the softmax needs no
-// per-score FMA; m_run is then kept in log2 units.
+// the accumulator value -m (four copies of the row's reference, built for
+// that MFMA) instead of 0 -- so the softmax needs no per-score FMA; m_run is
+// then kept in log2 units.
 template <bool PRE>
 __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-    const int h = lane >> 5;
+    const int g = lane >> 4;
 
     const int nqb = (a.sq + BQ - 1) / BQ;
     const int per_split = nqb * a.num_heads;
@@ -400,19 +446,27 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     const int skv = a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
     float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
     float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
+    const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
+    const int64_t lse_hs = a.lse_head_stride ? a.lse_head_stride : (int64_t)a.sq;
 
     const half_t *qh = a.q + (int64_t)head * a.q_head_stride;
-    const int q = qb * BQ + wave * 32 + (lane & 31);
-    const int qc = min(q, a.sq - 1);
-    half8 qf[8];
+    const int q0 = qb * BQ + wave * 16 * NQ;  // first query row of the wave
+    State st;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 16 + 8 * h));
-
-    floatx16 o[4], sa[2], sb[2];
+    for (int j = 0; j < NQ; ++j) {
+        const int qc = min(q0 + 16 * j + (lane & 15), a.sq - 1);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) o[mb] = floatx16{};
-    float m_run = -INFINITY, l_run = 0.0f;
-    floatx16 negm = floatx16{};  // PRE: accumulator start value -m of the S MFMAs
+        for (int kk = 0; kk < 4; ++kk) st.qf[j][kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 32 + 8 * g));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) st.o[mb][j] = floatx4{};
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        st.m_run[j] = -INFINITY;
+        st.l_run[j] = 0.0f;
+    }
 
     Ctx c;
     c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D);
@@ -423,126 +477,151 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     c.wave = wave;
     c.lane = lane;
     c.skv = skv;
+    c.NH = (skv + 31) / 32;
     c.T = (skv + BN - 1) / BN;
     c.vrs = a.v_row_stride;
     const int T = c.T;
 
     if (T > 0) {
+        SBlk sa, sb;
         issue_stage(c, -1);
         issue_stage(c, 0);
         issue_stage(c, 1);
         wait_vm_lgkm(issue_stage(c, 2));  // stages -1, 0, 1 complete
         barrier_no_fence();
         {
-            const half_t *k0 = c.rl + 3 * SLOT;
-            half8 fa[16];
+            // S of key half 0 from stage -1's second K half (slot 3)
+            const half_t *k0 = c.rl + 3 * SLOT + HFRAG * FRAG;
 #pragma unroll
-            for (int n = 0; n < 16; ++n) fa[n] = rd(k0 + n * FRAG);
-#pragma unroll
-            for (int n = 0; n < 16; ++n) {
+            for (int n = 0; n < 8; ++n) {
+                const half8 f = rd(k0 + n * FRAG);
                 const int kk = n >> 1, kb = n & 1;
-                sa[kb] = mfma32(fa[n], qf[kk], kk == 0 ? floatx16{} : sa[kb]);
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) sa[kb][j] = mfma16(f, st.qf[j][kk], kk == 0 ? floatx4{} : sa[kb][j]);
             }
         }
-        const float mt = (BN <= skv) ? row_max<false>(sa, 0, skv, h) : row_max<true>(sa, 0, skv, h);
+        float lm[NQ];
+        if (32 <= skv)
+            local_max<false>(sa, 0, skv, g, lm);
+        else
+            local_max<true>(sa, 0, skv, g, lm);
         if (PRE) {
-            // the first tile sets the reference: S_0 came out relative to 0
-            m_run = mt;
+            // the first half sets the reference: its scores came out relative to 0
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) sa[kb] -= mt;
-            negm = -mt;
+            for (int j = 0; j < NQ; ++j) {
+                const float mt = max_over_key_lanes(lm[j]);
+                st.m_run[j] = mt;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) sa[kb][j] -= mt;
+            }
         } else {
-            update_max(mt, m_run, l_run, o);
+            update_max(lm, st.m_run, st.l_run, st.o);
         }
-        // Step 0 refills slot 3: every wave must be done reading K_0.
+        // Step 0 refills slot 3: every wave must be done reading it.
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
         barrier_no_fence();
 
-        // Steady steps need stage t+3 full (t + 4 <= last full tile) and run
-        // in pairs, so the two S register sets swap roles without copies.
-        const int last_full = (skv % BN == 0) ? T - 1 : T - 2;
-        const int n_steady = max(0, last_full - 3);
+        // Step t is steady when stage t+3 is full: 64t + 288 <= skv.
+        const int n_steady = skv >= 288 ? (skv - 288) / BN + 1 : 0;
+        half8 fr[RA];
         int t = 0;
-        if (n_steady >= 2) {
-            half8 fr[RA];
+        if (n_steady > 0) {
 #pragma unroll
             for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
-            for (; t + 1 < n_steady; t += 2) {
-                steady_step<PRE>(c, t, sa, sb, o, qf, fr, m_run, l_run, negm);
-                steady_step<PRE>(c, t + 1, sb, sa, o, qf, fr, m_run, l_run, negm);
+            for (; t < n_steady; ++t) {
+                half_step<PRE, true, 0>(c, t, sa, sb, st, fr);
+                half_step<PRE, true, 1>(c, t, sb, sa, st, fr);
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
+                barrier_no_fence();
             }
         }
         for (; t < T; ++t) {
-            general_step<PRE>(c, t, sa, sb, o, qf, m_run, l_run, negm);
-            swap_s(sa, sb);
+            const int inflight = issue_stage(c, t + 3);
+            half_step<PRE, false, 0>(c, t, sa, sb, st, fr);
+            half_step<PRE, false, 1>(c, t, sb, sa, st, fr);
+            if (t + 1 < T) {
+                wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
+                barrier_no_fence();
+            }
         }
     }
 
-    // ---- epilogue: combine the two lane halves' sums, normalise, stage the
-    // wave's 32 x 128 block through LDS and store whole rows.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // ---- epilogue: combine the four lane groups' sums, normalise, stage the
+    // wave's rows through LDS and store whole rows.
     const bool empty = skv == 0;
-    const float inv = empty ? 0.0f : 1.0f / l_tot;
+    float inv[NQ], l_tot[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        float l = st.l_run[j];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        l_tot[j] = l;
+        inv[j] = empty ? 0.0f : 1.0f / l;
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
     barrier_no_fence();  // every wave is done with the ring
-    const int q0 = qb * BQ + wave * 32;
-    const int rows = min(32, a.sq - q0);
-    const int qr = lane & 31;
+    const int qr = lane & 15;
     if (o32) {
-        float *st = reinterpret_cast<float *>(smem) + wave * 32 * OP32;
+        float *stg = reinterpret_cast<float *>(smem) + wave * 16 * OP32;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int j = 0; j < NQ; ++j) {
+            const int qj = q0 + 16 * j;
+            const int rows = min(16, a.sq - qj);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                floatx4 v;
+            for (int mb = 0; mb < 8; ++mb)
+                *reinterpret_cast<floatx4 *>(stg + qr * OP32 + 16 * mb + 4 * g) = st.o[mb][j] * inv[j];
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+            __builtin_amdgcn_wave_barrier();
+            float *dst = o32 + (int64_t)head * o32_hs + (int64_t)qj * D;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) v[rr] = o[mb][4 * g + rr] * inv;
-                *reinterpret_cast<floatx4 *>(st + qr * OP32 + 32 * mb + 8 * g + 4 * h) = v;
+            for (int i = 0; i < 8; ++i) {
+                const int row = 2 * i + (lane >> 5), chunk = lane & 31;
+                if (row < rows)
+                    *reinterpret_cast<floatx4 *>(dst + (int64_t)row * D + 4 * chunk) =
+                        *reinterpret_cast<const floatx4 *>(stg + row * OP32 + 4 * chunk);
             }
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-        __builtin_amdgcn_wave_barrier();
-        float *dst = o32 + ((int64_t)head * a.sq + q0) * D;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 2 * i + (lane >> 5), chunk = lane & 31;
-            if (row < rows)
-                *reinterpret_cast<floatx4 *>(dst + (int64_t)row * D + 4 * chunk) =
-                    *reinterpret_cast<const floatx4 *>(st + row * OP32 + 4 * chunk);
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-        __builtin_amdgcn_wave_barrier();
     }
     if (a.o16) {
-        half_t *st = reinterpret_cast<half_t *>(smem) + wave * 32 * OP16;
+        half_t *stg = reinterpret_cast<half_t *>(smem) + wave * 16 * NQ * OP16;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int j = 0; j < NQ; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int mb = 0; mb < 8; ++mb) {
                 half4 v;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) v[rr] = (half_t)(o[mb][4 * g + rr] * inv);
-                *reinterpret_cast<half4 *>(st + qr * OP16 + 32 * mb + 8 * g + 4 * h) = v;
+                for (int r = 0; r < 4; ++r) v[r] = (half_t)(st.o[mb][j][r] * inv[j]);
+                *reinterpret_cast<half4 *>(stg + (16 * j + qr) * OP16 + 16 * mb + 4 * g) = v;
             }
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
         __builtin_amdgcn_wave_barrier();
+        const int rows = min(16 * NQ, a.sq - q0);
         half_t *dst = a.o16 + (int64_t)q0 * a.o16_ld + (int64_t)head * D;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4 * NQ; ++i) {
             const int row = 4 * i + (lane >> 4), chunk = lane & 15;
             if (row < rows)
                 *reinterpret_cast<u32x4 *>(dst + (int64_t)row * a.o16_ld + 8 * chunk) =
-                    *reinterpret_cast<const u32x4 *>(st + row * OP16 + 8 * chunk);
+                    *reinterpret_cast<const u32x4 *>(stg + row * OP16 + 8 * chunk);
         }
     }
-    if (lse_out && h == 0 && q < a.sq) {
-        // natural-log LSE; __builtin_amdgcn_logf is log2
-        const float lse = PRE ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2
-                              : m_run + __builtin_amdgcn_logf(l_tot) * kLn2;
-        lse_out[(int64_t)head * a.sq + q] = empty ? -INFINITY : lse;
+    if (lse_out && g == 0) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int q = q0 + 16 * j + qr;
+            if (q < a.sq) {
+                // natural-log LSE; __builtin_amdgcn_logf is log2
+                const float lse = PRE ? (st.m_run[j] + __builtin_amdgcn_logf(l_tot[j])) * kLn2
+                                      : st.m_run[j] + __builtin_amdgcn_logf(l_tot[j]) * kLn2;
+                lse_out[(int64_t)head * lse_hs + q] = empty ? -INFINITY : lse;
+            }
+        }
     }
 }
 
-// One workgroup per (key split, head, 256-row query block) item, remapped so
+// One workgroup per (key split, head, 384-row query block) item, remapped so
 // each XCD works through a contiguous range of items and its concurrent
 // workgroups share one head's K/V in L2.
 template <bool PRE>
@@ -562,6 +641,136 @@ hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     else
         hipLaunchKernelGGL(flash_fwd_f16_d128<false>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxSplit = 16;         // key ranges of a split tail
+constexpr int kMinSplitKeys = 512;    // shortest key range worth a workgroup
+// Cost model of a plan, in seconds: a workgroup over L keys takes about
+// kItemPerKey * L (384 rows at the kernel's rate on one CU) plus a fixed
+// start-up and epilogue kItemFixed; the partials of a split tail are written
+// once and read once by the merge at about kMergeBw; the two extra launches
+// cost kExtraLaunch.
+constexpr double kItemPerKey = 3.95e-8, kItemFixed = 8e-6, kMergeBw = 4.0e12, kExtraLaunch = 1.5e-5;
+
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (256 on an MI355X).
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace
+
+// The grid of a plain launch is H * ceil(sq / 384) workgroups of equal
+// length, run in rounds of one workgroup per CU; a last round that is only
+// partly full leaves CUs idle for a whole workgroup time (10% of the time at
+// 32 heads and seq 16384). The plan keeps the first query blocks of every
+// head whole and splits the last tb blocks of every head into k key ranges,
+// so the tail runs as short workgroups that fill their rounds; their
+// partials are merged by LSE. It takes the (tb, k) of least modelled time,
+// counting the merge traffic and the extra launches, and no split unless
+// that gains at least 1% over the plain launch.
+AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems) {
+    AttnPlan p{sq, 1, 0, 0, 0};
+    if (num_heads <= 0 || sq <= 0 || skv < 2 * kMinSplitKeys) return p;
+    const int64_t C = cu_count();
+    const int nqb = (sq + BQ - 1) / BQ;
+    const double t_item = kItemPerKey * skv + kItemFixed;
+    auto rounds = [C](int64_t n) { return (double)((n + C - 1) / C); };
+    const double plain = rounds((int64_t)nqb * num_heads) * t_item;
+    double best = 0.99 * plain;
+    const int tb_max = (int)std::min<int64_t>(nqb, 2 * C / num_heads + 1);
+    for (int tb = 1; tb <= nqb; ++tb) {
+        if (tb > tb_max && tb != nqb) continue;
+        const int main_rows = (nqb - tb) * BQ;
+        const int tail_rows = sq - main_rows;
+        for (int k = 2; k <= kMaxSplit; ++k) {
+            const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
+            if (len < kMinSplitKeys) break;
+            const int ke = (skv + len - 1) / len;
+            const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
+            if (o_el > max_o_elems) break;
+            const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
+            const double t = rounds((int64_t)(nqb - tb) * num_heads) * t_item +
+                             rounds((int64_t)tb * num_heads * ke) * (kItemPerKey * len + kItemFixed) + merge +
+                             kExtraLaunch;
+            if (t < best) {
+                best = t;
+                p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows};
+            }
+        }
+    }
+    return p;
+}
+
+hipError_t launch_attention_f16(const FlashArgs &a, const AttnPlan &p, float *ws_o, float *ws_lse,
+                                hipStream_t stream) {
+    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || (a.o16 && a.o32) || (!a.o16 && !a.o32) ||
+        !ws_o || !ws_lse)
+        return launch_flash_fwd_f16(a, stream);
+    hipError_t e = hipSuccess;
+    const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
+    const int64_t lse_hs = a.lse_head_stride ? a.lse_head_stride : (int64_t)a.sq;
+    if (p.main_rows > 0) {
+        FlashArgs m = a;
+        m.sq = p.main_rows;
+        m.o32_head_stride = o32_hs;
+        m.lse_head_stride = lse_hs;
+        e = launch_flash_fwd_f16(m, stream);
+        if (e != hipSuccess) return e;
+    }
+    const int tail = a.sq - p.main_rows;
+    FlashArgs t = a;
+    t.q = a.q + (int64_t)p.main_rows * D;
+    t.sq = tail;
+    t.o16 = nullptr;
+    t.o32 = ws_o;
+    t.lse = ws_lse;
+    t.o32_head_stride = 0;
+    t.lse_head_stride = 0;
+    t.n_split = p.n_split;
+    t.split_len = p.split_len;
+    e = launch_flash_fwd_f16(t, stream);
+    if (e != hipSuccess) return e;
+    MergeArgs mg{};
+    mg.n_parts = p.n_split;
+    mg.num_heads = a.num_heads;
+    mg.head_dim = D;
+    mg.sq = tail;
+    mg.o_parts = ws_o;
+    mg.lse_parts = ws_lse;
+    if (a.o16) {
+        mg.o_out = a.o16 + (int64_t)p.main_rows * a.o16_ld;
+        mg.o_ld = a.o16_ld;
+        mg.o_hs = D;
+        mg.out_f16 = 1;
+    } else {
+        mg.o_out = a.o32 + (int64_t)p.main_rows * D;
+        mg.o_ld = D;
+        mg.o_hs = o32_hs;
+        mg.out_f16 = 0;
+    }
+    if (a.lse) {
+        mg.lse_out = a.lse + p.main_rows;
+        mg.lse_hs = lse_hs;
+    }
+    return launch_lse_merge(mg, stream);
 }
 
 }  // namespace attnblk

@@ -16,7 +16,9 @@ namespace attnblk {
 //   k   (j,t,c) at k[j*k_head_stride + t*D + c], t < skv
 //   vt  (j,c,t) at vt[j*v_head_stride + c*v_row_stride + t]
 // Outputs (any may be null): o16/otok token-major [sq][o16_ld] in the path's
-// dtype at column head*D; o32 fp32 [H][sq][D]; lse fp32 [H][sq].
+// dtype at column head*D; o32 fp32 head-major, row (j, i) at
+// o32 + j*o32_head_stride + i*D; lse fp32 at lse[j*lse_head_stride + i]. A
+// head stride of 0 means the packed layout ([H][sq][D], [H][sq]).
 struct FlashArgs {
     const _Float16 *q;
     const _Float16 *k;
@@ -27,9 +29,11 @@ struct FlashArgs {
     int64_t o16_ld;
     float *o32;
     float *lse;
+    int64_t o32_head_stride, lse_head_stride;
     // Key split (0 or 1: none): workgroup item w covers split w / (H * query
     // blocks), keys [split * split_len, min(skv, (split + 1) * split_len)),
-    // and writes its partial o32 / lse at split * H * sq * d / split * H * sq.
+    // and writes its partial o32 / lse at split * H * sq * d / split * H * sq
+    // (packed layout; the head strides must be 0).
     int n_split, split_len;
     // Non-zero: q holds q_scaled * log2(e) (the block's internal Q), so the
     // softmax works in base 2 with no per-score multiply.
@@ -116,11 +120,41 @@ struct MergeArgs {
     const float *lse_parts;
     void *o_out;
     int64_t o_ld;  // row stride of o_out (elements); 0 means num_heads * head_dim
+    int64_t o_hs;  // head stride of o_out (elements); 0 means head_dim (heads side by side)
     int out_f16;
     float *lse_out;
+    int64_t lse_hs;  // head stride of lse_out; 0 means sq
 };
 
+// Launch plan of one fp16 attention (flash_fwd.hip): the query rows
+// [0, main_rows) of every head run as whole-key workgroups; the rows
+// [main_rows, sq) run split into n_split key ranges of split_len keys, whose
+// fp32 partials (o_elems and lse_elems floats of workspace) are then merged
+// into the outputs. n_split <= 1: one plain launch.
+struct AttnPlan {
+    int main_rows, n_split, split_len;
+    int64_t o_elems, lse_elems;
+};
+
+// Workspace budgets of a key-split attention tail (floats of partial rows):
+// the block's own workspace, and the one every rank-share partial entry point
+// plans with (pool, fixed array or ring alike, so that they all choose the
+// same plan and give the same bits).
+constexpr int64_t kSplitWsFloats = int64_t(64) << 20;
+constexpr int64_t kPartialWsFloats = int64_t(16) << 20;
+
+// The library's stream-ordered memory pool on the current device
+// (partial.hip): memory freed on a stream stays in the pool for later calls.
+hipError_t staging_pool(hipMemPool_t *out);
+
 hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream);
+// Plan for num_heads heads, sq query rows and skv keys whose split workspace
+// holds at most max_o_elems floats of partial rows.
+AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems);
+// The attention of `a` (n_split 0; outputs o16 or o32, and lse) by plan p,
+// with ws_o / ws_lse holding p.o_elems / p.lse_elems floats when p splits.
+hipError_t launch_attention_f16(const FlashArgs &a, const AttnPlan &p, float *ws_o, float *ws_lse,
+                                hipStream_t stream);
 hipError_t launch_flash_fwd_f32(const FlashArgsF32 &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgsF32 &a, hipStream_t stream);

@@ -4,9 +4,10 @@
 // Multi-Device Inference Support", three context-parallel implementations):
 //   M = max_b lse_b, w_b = exp(lse_b - M), lse = M + ln sum_b w_b,
 //   o = (sum_b w_b o_b) / sum_b w_b.
-// Output rows are written token-major [sq][H*d] -- the concatenated-heads
-// layout the output projection reads ("Tensor Parallelism: Sharding Weights
-// for Parallel Layer Execution", section 3).
+// Output rows are written token-major [sq][H*d] by default -- the
+// concatenated-heads layout the output projection reads ("Tensor Parallelism:
+// Sharding Weights for Parallel Layer Execution", section 3) -- or with any
+// row and head strides.
 //
 // HBM-bound: each thread owns four consecutive head dimensions of one
 // (head, query) row, so every part is read in 16-byte coalesced chunks (four
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
         acc *= 1.0f / total;
         lse = m + logf(total);
     }
-    const int64_t ocol = (int64_t)head * a.head_dim + 4 * t;
+    const int64_t ocol = (int64_t)head * (a.o_hs ? a.o_hs : a.head_dim) + 4 * t;
     const int64_t ld = a.o_ld ? a.o_ld : (int64_t)a.num_heads * a.head_dim;
     if (a.out_f16) {
         half4 hv;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
     } else {
         *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(a.o_out) + q * ld + ocol) = acc;
     }
-    if (a.lse_out && t == 0) a.lse_out[row] = lse;
+    if (a.lse_out && t == 0) a.lse_out[(int64_t)head * (a.lse_hs ? a.lse_hs : a.sq) + q] = lse;
 }
 
 }  // namespace

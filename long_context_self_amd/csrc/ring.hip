@@ -16,6 +16,7 @@
 // may be device memory or pinned host memory (hipMemcpyAsync with
 // hipMemcpyDefault), standing in for a peer's link.
 
+#include <algorithm>
 #include <cstring>
 
 #include "attn_block.h"
@@ -32,6 +33,8 @@ struct attn_ring {
     void *slot_k[2], *slot_vt[2];  // K [H][len][d], V^T [H][d][ATTN_VT_LD(len)] of the block in the slot
     float *o_parts;                // [n_blocks][H][max_sq][d] (each block's part packed for the sq of a call)
     float *lse_parts;              // [n_blocks][H][max_sq]
+    float *split_ws;               // fp16: partials of a block's split tail (plan_attention_f16), split_elems floats
+    int64_t split_elems;
     hipStream_t copy;
     hipEvent_t start, arrived[2], freed[2];
 };
@@ -40,7 +43,7 @@ namespace {
 
 void free_ring(attn_ring *r) {
     if (!r) return;
-    void *ptrs[] = {r->slot_k[0], r->slot_k[1], r->slot_vt[0], r->slot_vt[1], r->o_parts, r->lse_parts};
+    void *ptrs[] = {r->slot_k[0], r->slot_k[1], r->slot_vt[0], r->slot_vt[1], r->o_parts, r->lse_parts, r->split_ws};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     hipEvent_t evs[] = {r->start, r->arrived[0], r->arrived[1], r->freed[0], r->freed[1]};
@@ -82,6 +85,9 @@ ATTN_API attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int he
     r->max_block = max_block_len;
     hipError_t e = hipGetDevice(&r->device);
     const size_t es = elem_size(r->dt), hd = (size_t)num_heads * head_dim;
+    // the partial entry points' budget; rows plus one LSE per head_dim of them
+    if (r->dt == kF16)
+        r->split_elems = std::min<int64_t>(kPartialWsFloats, 16 * (int64_t)hd * max_sq) * (head_dim + 1) / head_dim;
     struct {
         void **p;
         size_t bytes;
@@ -90,9 +96,11 @@ ATTN_API attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int he
                   {&r->slot_vt[0], hd * ATTN_VT_LD(max_block_len) * es},
                   {&r->slot_vt[1], hd * ATTN_VT_LD(max_block_len) * es},
                   {reinterpret_cast<void **>(&r->o_parts), (size_t)n_blocks * hd * max_sq * sizeof(float)},
-                  {reinterpret_cast<void **>(&r->lse_parts), (size_t)n_blocks * num_heads * max_sq * sizeof(float)}};
+                  {reinterpret_cast<void **>(&r->lse_parts), (size_t)n_blocks * num_heads * max_sq * sizeof(float)},
+                  {reinterpret_cast<void **>(&r->split_ws), (size_t)r->split_elems * sizeof(float)}};
     for (auto &a : allocs) {
         if (e != hipSuccess) break;
+        if (a.bytes == 0) continue;
         e = hipMalloc(a.p, a.bytes);
         if (e != hipSuccess) {
             *a.p = nullptr;
@@ -177,7 +185,11 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
             fa.num_heads = H;
             fa.o32 = ob;
             fa.lse = lb;
-            HIP_TRY("attn_ring_forward: partial", launch_flash_fwd_f16(fa, stream));
+            // the plan of attn_partial_forward_vt for the same shape, so the
+            // ring equals partials + merge bit for bit
+            const AttnPlan plan = plan_attention_f16(H, (int)sq, (int)len, kPartialWsFloats);
+            HIP_TRY("attn_ring_forward: partial",
+                    launch_attention_f16(fa, plan, ring->split_ws, ring->split_ws + plan.o_elems, stream));
         } else {
             FlashArgsF32 fa{};
             fa.q = static_cast<const float *>(q_scaled);

@@ -44,6 +44,25 @@ def test_partial_f16_vs_oracle(h, sq, skv):
     assert_close(lse, lse_ref, what="lse_part")
 
 
+def test_planned_split_tail_vs_oracle():
+    # 32 heads, 3500 query rows: 320 workgroups of 384 rows would leave the
+    # second round of 256 CUs mostly idle, so the launch plan runs rows
+    # [0, 3072) whole and splits the last 428 rows of every head over key
+    # ranges, merged by LSE. Both parts, and the border between them, against
+    # the oracle on two heads (all rows).
+    h, sq, skv, d = 32, 3500, 3500, 128
+    say(f"planned launch with a split tail: H={h} sq={sq} skv={skv}")
+    q, k, v = attention_inputs(h, sq, skv, d, seed=9)
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    heads = [0, h - 1]
+    o_ref, lse_ref = oracle.partial_attention(q[heads], k[heads], v[heads])
+    assert_close(host(o)[heads], o_ref, what="o_part (whole rows and split tail)")
+    assert_close(host(lse)[heads], lse_ref, what="lse_part (whole rows and split tail)")
+    o2, lse2 = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "planned launch not deterministic"
+
+
 def test_partial_f16_peaked_scores_exercise_rescale():
     # score std 8: running maxima keep growing by more than the 2^8 lazy-rescale threshold
     say("partial f16 peaked scores")
@@ -168,8 +187,11 @@ def test_merge_ignores_empty_parts_and_handles_all_empty():
 @pytest.mark.parametrize("a,b", [(256, 512), (100, 357), (999, 1000)])
 def test_row_chunk_is_bit_exact(a, b):
     # Rows [a, b) run alone against the full K/V equal rows [a, b) of the full run.
+    # Below 1024 keys no launch plan splits keys, so both runs are plain launches
+    # and every row's arithmetic is the kernel's alone (with a split tail, rows
+    # in it are summed in another order, and which rows fall there depends on sq).
     say(f"row chunk [{a},{b}) bit-exact")
-    h, sq, skv, d = 2, 1000, 1500, 128
+    h, sq, skv, d = 2, 1000, 1000, 128
     q, k, v = attention_inputs(h, sq, skv, d, seed=7)
     kd, vt = dev(k), to_vt(v)
     vtd = dev(vt)

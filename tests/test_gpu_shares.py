@@ -114,7 +114,9 @@ def test_ulysses_share_small_all_rows():
 
 
 def test_ulysses_all_ranks_equal_one_shot_attention():
-    n, hh, s, d = 8, 16, 1024, 128
+    # Below 1024 keys no launch plan splits keys, so the share of any head
+    # count runs the same per-row arithmetic as the one-shot call.
+    n, hh, s, d = 8, 16, 960, 128
     say(f"Ulysses: all {n} ranks' shares vs one attention over all {hh} heads (bit-exact)")
     q, k, v = attention_inputs(hh, s, s, d, seed=22)
     vt = _vt(v)
