@@ -62,7 +62,7 @@ constexpr int FRAG = 64 * 8;          // halves in one MFMA operand fragment
 constexpr int HFRAG = 16;             // fragments per half-stage: 8 of K, then 8 of V^T
 constexpr int SLOT = 2 * HFRAG * FRAG;    // halves per ring slot
 constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
-constexpr int RA = 2;                     // operand reads in flight ahead of the MFMAs
+constexpr int RA = 3;                     // operand reads in flight ahead of the MFMAs
 constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
 constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
 constexpr int OSTAGE16 = NWAVES * 16 * NQ * OP16 * 2;
@@ -383,10 +383,10 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
             a = fr[n % RA];
             const int m = U * HFRAG + n + RA;
             fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
-            // stage t+3's direct loads go out a quarter of the way into each
-            // half-step rather than in one burst at the step's start
-            if (U == 0 && n == 4) issue_k_full(c, t + 3);
-            if (U == 1 && n == 4) issue_v_full(c, t + 3);
+            // stage t+3's direct loads go out halfway into each half-step
+            // (K, then V^T) rather than in one burst at the step's start
+            if (U == 0 && n == 8) issue_k_full(c, t + 3);
+            if (U == 1 && n == 8) issue_v_full(c, t + 3);
         } else {
             a = rd(cur + (U * HFRAG + n) * FRAG);
         }
