@@ -685,11 +685,13 @@ def main() -> int:
     kernel_tflops = {n: fl[n] / (kern[n]["mean"] * 1e-3) / 1e12 for n in ("qkv", "attn", "oproj")}
     dom = max(("qkv", "attn", "oproj"), key=lambda n: kern[n]["mean"])
     names = {"qkv": "gemm_f16_nt (QKV projection, fused layout epilogue)",
-             "attn": "flash_fwd_f16_d128 (attention)", "oproj": "gemm_f16_nt (output projection)"}
+             "attn": "attention step: flash_fwd_f16_d128 over the whole-key query blocks, then over the "
+                     "key-split tail rows, then lse_merge of that tail (one launch when the plan does not split)",
+             "oproj": "gemm_f16_nt (output projection)"}
     counters = f"hbm_counters_seq{seq}_h{h}.txt"
     roofline = {"bound": "mfma", "kernel": names[dom], "achieved": kernel_tflops[dom], "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": kernel_tflops[dom] / PEAK_F16_TFLOPS,
-                "traffic": hbm_traffic("flash_fwd_f16_d128", ("flash_fwd.hip", "common.hpp"), counters)
+                "traffic": hbm_traffic("attention", ("flash_fwd.hip", "common.hpp", "lse_merge.hip"), counters)
                 if dom == "attn" else None,
                 "flops_per_launch": fl[dom], "avg_launch_ms": kern[dom]["mean"],
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated, "
