@@ -384,8 +384,9 @@ def run_tp_share(torch, B, hip, warmup, steps, seq=8192, h=4096, nh=32, ranks=8,
 def run_ring_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks=8, seed=0):
     """Rank 0 of 8 with Ring-style streaming: its 4096-row query chunk against 8 K/V blocks of 4096 keys that
     arrive by copy from pinned host memory (a stand-in for a peer's link) on the ring's copy stream while the
-    earlier blocks' attention runs. Reported beside the same work with K/V already resident (compute only) and
-    the copies alone (transfer only)."""
+    earlier blocks' attention runs. Reported beside the same blocks already in device memory (the ring then
+    computes every block's partial in one launch), the per-block partial calls and merge with K/V resident
+    (compute only), and the copies alone (transfer only)."""
     from long_context_self_amd.synthetic import block_inputs
 
     d, ch = h // nh, seq // ranks
@@ -737,6 +738,7 @@ def main() -> int:
         log("ring streaming (rank 0 of 8), seq 32768, K/V blocks from pinned host memory")
         extra.append(run_ring_share(torch, B, hip, warmup, steps))
         log(f"  {extra[-1]['ms']:.3f} ms (compute only {extra[-1]['compute_only_ms']['median']:.3f}, device blocks "
+            f"in one launch "
             f"{extra[-1]['ring_device_blocks_ms']['median']:.3f}, transfer only "
             f"{extra[-1]['transfer_only_ms']['median']:.3f} at {extra[-1]['transfer_gbs']:.0f} GB/s), overlap "
             f"efficiency {extra[-1]['overlap_efficiency']:.2f}")

@@ -412,7 +412,13 @@ attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, a
  * each copied block's arrival. The copies of
  * a call start after the work already enqueued on `stream`; calls on one ring
  * must use one stream (or be ordered by the caller). The result equals
- * attn_partial_forward over each block followed by attn_merge_lse.
+ * attn_partial_forward over each block followed by attn_merge_lse, bit for bit
+ * when some block must be copied. When every block already sits in this
+ * device's memory (fp16, n_blocks <= 16) one launch computes all the blocks'
+ * partials, each block over its whole key range; the result then equals the
+ * per-block calls bit for bit below 1024 keys per block, and within the
+ * split-merge gate otherwise (the per-block calls may split a block's last
+ * query rows over key ranges).
  */
 attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled, int64_t sq,
                                 const void *const *k_blocks, const void *const *vt_blocks,

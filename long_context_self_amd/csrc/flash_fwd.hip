@@ -62,13 +62,17 @@ constexpr int FRAG = 64 * 8;          // halves in one MFMA operand fragment
 constexpr int HFRAG = 16;             // fragments per half-stage: 8 of K, then 8 of V^T
 constexpr int SLOT = 2 * HFRAG * FRAG;    // halves per ring slot
 constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
-constexpr int RA = 3;                     // operand reads in flight ahead of the MFMAs
+constexpr int RA = 2;                     // operand reads in flight ahead of the MFMAs
 constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
 constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
 constexpr int OSTAGE16 = NWAVES * 16 * NQ * OP16 * 2;
 constexpr int OSTAGE32 = NWAVES * 16 * OP32 * 4;
 constexpr int SMEM_BYTES = RING_BYTES;
 static_assert(OSTAGE16 <= RING_BYTES && OSTAGE32 <= RING_BYTES, "O staging reuses the ring");
+// The read-ahead registers are used round-robin by fragment index within a
+// half-step; the rotation carries over half-step and stage boundaries only
+// when it divides the fragments of a half-step.
+static_assert(HFRAG % RA == 0, "read-ahead must divide the fragments of a half-step");
 constexpr float kRescaleTau = 8.0f * kLn2;  // rescale only when a max grows by > 2^8
 
 // v_mfma_f32_16x16x32_f16: C[16x16] += A[16x32] * B[32x16]. Lane l supplies A
@@ -98,7 +102,7 @@ struct LoadOffsets {
     uint32_t k[2], v[2];  // bytes from the stage's first key of that kind
 };
 
-__device__ __forceinline__ LoadOffsets load_offsets(const FlashArgs &a, int wave, int lane) {
+__device__ __forceinline__ LoadOffsets load_offsets(int64_t v_row_stride, int wave, int lane) {
     const int r = lane & 15, g = lane >> 4;
     LoadOffsets o;
 #pragma unroll
@@ -107,7 +111,7 @@ __device__ __forceinline__ LoadOffsets load_offsets(const FlashArgs &a, int wave
         const int u = f >> 3, n = f & 7;
         const int kk = n >> 1, kb = n & 1;
         o.k[e] = (uint32_t)(((32 * u + kperm(kb, r)) * D + 32 * kk + 8 * g) * 2);
-        o.v[e] = (uint32_t)(((int64_t)(16 * n + r) * a.v_row_stride + 32 * u + 8 * g) * 2);
+        o.v[e] = (uint32_t)(((int64_t)(16 * n + r) * v_row_stride + 32 * u + 8 * g) * 2);
     }
     return o;
 }
@@ -383,10 +387,10 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
             a = fr[n % RA];
             const int m = U * HFRAG + n + RA;
             fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
-            // stage t+3's direct loads go out halfway into each half-step
-            // (K, then V^T) rather than in one burst at the step's start
-            if (U == 0 && n == 8) issue_k_full(c, t + 3);
-            if (U == 1 && n == 8) issue_v_full(c, t + 3);
+            // stage t+3's direct loads go out a quarter of the way into each
+            // half-step (K, then V^T) rather than in one burst at the step's start
+            if (U == 0 && n == 4) issue_k_full(c, t + 3);
+            if (U == 1 && n == 4) issue_v_full(c, t + 3);
         } else {
             a = rd(cur + (U * HFRAG + n) * FRAG);
         }
@@ -439,11 +443,18 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
 
     const int nqb = (a.sq + BQ - 1) / BQ;
     const int per_split = nqb * a.num_heads;
-    const int split = a.n_split > 1 ? work / per_split : 0;
+    // a key split, or one of several K/V blocks (both give a packed partial per part)
+    const int split = (a.n_split > 1 || a.n_kv_blocks > 0) ? work / per_split : 0;
     const int head = (work - split * per_split) / nqb;
     const int qb = (work - split * per_split) % nqb;
-    const int key_base = split * a.split_len;
-    const int skv = a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
+    const int key_base = a.n_split > 1 ? split * a.split_len : 0;
+    const bool blocks = a.n_kv_blocks > 0;
+    const int skv = blocks ? a.kv_len[split] : a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
+    const half_t *kbase = blocks ? a.kv_k[split] + (int64_t)head * a.kv_k_head_stride[split]
+                                 : a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D;
+    const half_t *vbase = blocks ? a.kv_vt[split] + (int64_t)head * a.kv_v_head_stride[split]
+                                 : a.vt + (int64_t)head * a.v_head_stride + key_base;
+    const int64_t vrs = blocks ? a.kv_v_row_stride[split] : a.v_row_stride;
     float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
     float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
     const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
@@ -469,17 +480,17 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     }
 
     Ctx c;
-    c.kh = reinterpret_cast<const char *>(a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D);
-    c.vh = reinterpret_cast<const char *>(a.vt + (int64_t)head * a.v_head_stride + key_base);
+    c.kh = reinterpret_cast<const char *>(kbase);
+    c.vh = reinterpret_cast<const char *>(vbase);
     c.ring = smem;
     c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
-    c.lo = load_offsets(a, wave, lane);
+    c.lo = load_offsets(vrs, wave, lane);
     c.wave = wave;
     c.lane = lane;
     c.skv = skv;
     c.NH = (skv + 31) / 32;
     c.T = (skv + BN - 1) / BN;
-    c.vrs = a.v_row_stride;
+    c.vrs = vrs;
     const int T = c.T;
 
     if (T > 0) {
@@ -635,7 +646,8 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     if (a.sq <= 0) return hipSuccess;
     const int nqb = (a.sq + BQ - 1) / BQ;
-    const int blocks = nqb * a.num_heads * (a.n_split > 1 ? a.n_split : 1);
+    const int parts = a.n_kv_blocks > 0 ? a.n_kv_blocks : a.n_split > 1 ? a.n_split : 1;
+    const int blocks = nqb * a.num_heads * parts;
     if (a.q_log2e)
         hipLaunchKernelGGL(flash_fwd_f16_d128<true>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
     else
@@ -721,8 +733,8 @@ AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems)
 
 hipError_t launch_attention_f16(const FlashArgs &a, const AttnPlan &p, float *ws_o, float *ws_lse,
                                 hipStream_t stream) {
-    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || (a.o16 && a.o32) || (!a.o16 && !a.o32) ||
-        !ws_o || !ws_lse)
+    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || a.n_kv_blocks > 0 || (a.o16 && a.o32) ||
+        (!a.o16 && !a.o32) || !ws_o || !ws_lse)
         return launch_flash_fwd_f16(a, stream);
     hipError_t e = hipSuccess;
     const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;

@@ -10,6 +10,9 @@
 
 namespace attnblk {
 
+// Most K/V blocks one fp16 attention launch takes (FlashArgs::n_kv_blocks).
+constexpr int kMaxKvBlocks = 16;
+
 // Attention over one key range for every head (fp16 path: head_dim 128;
 // fp32 path: head_dim 64 or 128). Elements are of the path's dtype.
 //   q   (j,i,c) at q[j*q_head_stride + i*D + c], i < sq
@@ -38,6 +41,15 @@ struct FlashArgs {
     // Non-zero: q holds q_scaled * log2(e) (the block's internal Q), so the
     // softmax works in base 2 with no per-score multiply.
     int q_log2e;
+    // Separate K/V blocks (n_kv_blocks > 0; n_split must be 0): workgroup item w
+    // covers block b = w / (H * query blocks), whose K and V^T are given by the
+    // b-th entries below (k/vt and their strides above are then unused), and
+    // writes its partial o32 / lse at b * H * sq * d / b * H * sq (packed).
+    int n_kv_blocks;
+    const _Float16 *kv_k[kMaxKvBlocks];
+    const _Float16 *kv_vt[kMaxKvBlocks];
+    int64_t kv_k_head_stride[kMaxKvBlocks], kv_v_head_stride[kMaxKvBlocks], kv_v_row_stride[kMaxKvBlocks];
+    int kv_len[kMaxKvBlocks];
 };
 
 struct FlashArgsF32 {

@@ -142,6 +142,46 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
     if (sq == 0) return ATTN_OK;
     const int H = ring->heads, d = ring->head_dim, nb = ring->n_blocks;
     const size_t es = elem_size(ring->dt);
+    MergeArgs m{};
+    m.n_parts = nb;
+    m.num_heads = H;
+    m.head_dim = d;
+    m.sq = sq;
+    m.o_parts = ring->o_parts;
+    m.lse_parts = ring->lse_parts;
+    m.o_out = o_out;
+    m.out_f16 = ring->dt == kF16;
+    m.lse_out = lse_out;
+    // Every block already in this device's memory: one launch computes all the
+    // blocks' partials as workgroups over (block, head, query rows). The 8
+    // blocks of a rank share then fill whole rounds of the CUs, where 8 launches
+    // of one block each leave part of a round idle.
+    bool all_resident = ring->dt == kF16 && nb <= kMaxKvBlocks;
+    for (int b = 0; b < nb && all_resident; ++b)
+        all_resident = block_lens[b] == 0 || (on_device(k_blocks[b], ring->device) &&
+                                              on_device(vt_blocks[b], ring->device));
+    if (all_resident) {
+        FlashArgs fa{};
+        fa.q = static_cast<const _Float16 *>(q_scaled);
+        fa.q_head_stride = sq * d;
+        fa.sq = (int)sq;
+        fa.num_heads = H;
+        fa.o32 = ring->o_parts;
+        fa.lse = ring->lse_parts;
+        fa.n_kv_blocks = nb;
+        for (int b = 0; b < nb; ++b) {
+            const int64_t len = block_lens[b], ld = ATTN_VT_LD(len);
+            fa.kv_k[b] = static_cast<const _Float16 *>(k_blocks[b]);
+            fa.kv_vt[b] = static_cast<const _Float16 *>(vt_blocks[b]);
+            fa.kv_k_head_stride[b] = len * d;
+            fa.kv_v_head_stride[b] = (int64_t)d * ld;
+            fa.kv_v_row_stride[b] = ld;
+            fa.kv_len[b] = (int)len;
+        }
+        HIP_TRY("attn_ring_forward: partials", launch_flash_fwd_f16(fa, stream));
+        HIP_TRY("attn_ring_forward: merge", launch_lse_merge(m, stream));
+        return ATTN_OK;
+    }
     // copies of this call start after the work already on `stream` (q, the caller's
     // buffers, and an earlier call's use of the slots)
     HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->start, stream));
@@ -209,16 +249,6 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
         }
         HIP_TRY("attn_ring_forward: hipEventRecord", hipEventRecord(ring->freed[slot], stream));
     }
-    MergeArgs m{};
-    m.n_parts = nb;
-    m.num_heads = H;
-    m.head_dim = d;
-    m.sq = sq;
-    m.o_parts = ring->o_parts;
-    m.lse_parts = ring->lse_parts;
-    m.o_out = o_out;
-    m.out_f16 = ring->dt == kF16;
-    m.lse_out = lse_out;
     HIP_TRY("attn_ring_forward: merge", launch_lse_merge(m, stream));
     return ATTN_OK;
 }

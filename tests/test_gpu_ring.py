@@ -18,7 +18,7 @@ import oracle
 from long_context_self_amd import binding as B
 from long_context_self_amd.synthetic import attention_inputs, block_inputs, sample_rows
 
-from .gpu_util import REL_L2_F32, assert_close, dev, host, say
+from .gpu_util import REL_L2_F32, REL_L2_SPLIT, assert_close, dev, host, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -115,6 +115,30 @@ def test_ring_tiny_fp32():
     o_ref, lse_ref = oracle.partial_attention(q, k, v)
     assert_close(host(o).reshape(sq, hh, d).transpose(1, 0, 2), o_ref, rel=REL_L2_F32, mabs=1e-5, what="O")
     assert_close(host(lse), lse_ref, rel=REL_L2_F32, mabs=1e-5, what="LSE")
+
+
+def test_ring_device_resident_blocks_one_launch():
+    # Every block in device memory: one launch over (block, head, query rows) for
+    # all blocks. Blocks of 1024 keys or more may be split by the per-block calls'
+    # plan, so the two agree within the split-merge gate; both meet the oracle's.
+    hh, sq, d = 8, 1000, 128
+    lens = [2048, 1500, 0, 3000, 64]
+    say(f"ring, device-resident blocks {lens}, H={hh} sq={sq}")
+    q, k, v = attention_inputs(hh, sq, sum(lens), d, seed=45)
+    kb, vb = _blocks(k, v, lens)
+    qd = dev(q)
+    o, lse = _ring(qd, sq, kb, vb, lens, hh, d)
+    o_ref, lse_ref = oracle.partial_attention(q[:2], k[:2], v[:2])
+    got = host(o).reshape(sq, hh, d).transpose(1, 0, 2)
+    assert_close(got[:2], o_ref, what="ring O (one launch)")
+    assert_close(host(lse)[:2], lse_ref, what="ring LSE (one launch)")
+    o2, lse2 = _sequential(qd, sq, kb, vb, lens, hh, d)
+    r = rel_l2(host(o).astype(np.float64), host(o2).astype(np.float64))
+    say(f"  one launch vs per-block partials + merge: rel_l2={r:.2e}")
+    assert r <= REL_L2_SPLIT
+    assert rel_l2(host(lse), host(lse2)) <= REL_L2_SPLIT
+    o3, lse3 = _ring(qd, sq, kb, vb, lens, hh, d)
+    assert torch.equal(o, o3) and torch.equal(lse, lse3), "one-launch ring not deterministic"
 
 
 def test_ring_config_seq32768_rank0_pinned():
