@@ -414,11 +414,14 @@ attn_status_t attn_ring_create(attn_ring_t **out, int num_heads, int head_dim, a
  * must use one stream (or be ordered by the caller). The result equals
  * attn_partial_forward over each block followed by attn_merge_lse, bit for bit
  * when some block must be copied. When every block already sits in this
- * device's memory (fp16, n_blocks <= 16) one launch computes all the blocks'
- * partials, each block over its whole key range; the result then equals the
- * per-block calls bit for bit below 1024 keys per block, and within the
- * split-merge gate otherwise (the per-block calls may split a block's last
- * query rows over key ranges).
+ * device's memory (fp16, n_blocks <= 16) one launch does the work: blocks of
+ * one power-of-two length (>= 64) are read as a single key sequence (the
+ * result equals attn_partial_forward_vt over the concatenated K/V, rounded to
+ * fp16, bit for bit); other blocks get one partial each, each over its whole
+ * key range, then the merge (equal to the per-block calls bit for bit below
+ * 1024 keys per block). Either way the result meets the split-merge gate
+ * against the per-block calls, whose plans may split a block's last query
+ * rows over key ranges.
  */
 attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled, int64_t sq,
                                 const void *const *k_blocks, const void *const *vt_blocks,

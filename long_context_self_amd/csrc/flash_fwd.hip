@@ -102,7 +102,10 @@ struct LoadOffsets {
     uint32_t k[2], v[2];  // bytes from the stage's first key of that kind
 };
 
-__device__ __forceinline__ LoadOffsets load_offsets(int64_t v_row_stride, int wave, int lane) {
+// half_base: the K base the loads add these to is the first key of the
+// wave's own half (CAT), not of the stage's K part, so the half's 32 keys are
+// left out of the K offsets.
+__device__ __forceinline__ LoadOffsets load_offsets(int64_t v_row_stride, int wave, int lane, bool half_base) {
     const int r = lane & 15, g = lane >> 4;
     LoadOffsets o;
 #pragma unroll
@@ -110,7 +113,7 @@ __device__ __forceinline__ LoadOffsets load_offsets(int64_t v_row_stride, int wa
         const int f = 2 * wave + e;  // 0..15
         const int u = f >> 3, n = f & 7;
         const int kk = n >> 1, kb = n & 1;
-        o.k[e] = (uint32_t)(((32 * u + kperm(kb, r)) * D + 32 * kk + 8 * g) * 2);
+        o.k[e] = (uint32_t)((((half_base ? 0 : 32 * u) + kperm(kb, r)) * D + 32 * kk + 8 * g) * 2);
         o.v[e] = (uint32_t)(((int64_t)(16 * n + r) * v_row_stride + 32 * u + 8 * g) * 2);
     }
     return o;
@@ -123,7 +126,35 @@ struct Ctx {
     LoadOffsets lo;
     int wave, lane, skv, NH, T;  // NH: 32-key halves, T: stages
     int64_t vrs;
+    // CAT (keys in equal blocks of 2^lg_len, read as one sequence): the block
+    // table, this item's head and its first key in that sequence
+    const FlashArgs *a;
+    int head, key_base, lg_len;
 };
+
+// This head's K row and V^T column of the first key of 32-key half `half`
+// (bytes). CAT: the key lies in block (key_base + 32 half) >> lg_len; a half
+// never straddles two blocks, whose length is a multiple of 64.
+template <bool CAT>
+__device__ __forceinline__ const char *k_half(const Ctx &c, int half) {
+    if constexpr (CAT) {
+        const int key = c.key_base + 32 * half, b = key >> c.lg_len;
+        return reinterpret_cast<const char *>(c.a->kv_k[b] + (int64_t)c.head * c.a->kv_k_head_stride[b] +
+                                              (int64_t)(key - (b << c.lg_len)) * D);
+    } else {
+        return c.kh + (int64_t)half * 32 * D * 2;
+    }
+}
+template <bool CAT>
+__device__ __forceinline__ const char *v_half(const Ctx &c, int half) {
+    if constexpr (CAT) {
+        const int key = c.key_base + 32 * half, b = key >> c.lg_len;
+        return reinterpret_cast<const char *>(c.a->kv_vt[b] + (int64_t)c.head * c.a->kv_v_head_stride[b] +
+                                              (key - (b << c.lg_len)));
+    } else {
+        return c.vh + (int64_t)half * 32 * 2;
+    }
+}
 
 // LDS byte address of the e-th fragment of kind K (0) or V^T (1) that this
 // wave loads, in the slot of stage s.
@@ -140,17 +171,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, -1, 0x00020000);
 }
 
-// K of stage s >= 0 (keys 64s + 32 .. 64s + 96, all present) -> slot s.
+// K of stage s >= 0 (keys 64s + 32 .. 64s + 96, all present) -> slot s. The
+// wave's two fragments lie in one 32-key half, 2s + 1 + wave / 4.
+template <bool CAT>
 __device__ __forceinline__ void issue_k_full(const Ctx &c, int s) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.kh + ((int64_t)s * BN + 32) * D * 2);
+    const __amdgpu_buffer_rsrc_t r =
+        CAT ? tile_rsrc(k_half<CAT>(c, 2 * s + 1 + (c.wave >> 2))) : tile_rsrc(c.kh + ((int64_t)s * BN + 32) * D * 2);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)frag_dst(c, s, 0, e), 16, c.lo.k[e], 0, 0, 0);
 }
 
 // V^T of stage s >= 0 (keys 64s .. 64s + 64, all present) -> slot s.
+template <bool CAT>
 __device__ __forceinline__ void issue_v_full(const Ctx &c, int s) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(c.vh + (int64_t)s * BN * 2);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(v_half<CAT>(c, 2 * s));
 #pragma unroll
     for (int e = 0; e < 2; ++e)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)frag_dst(c, s, 1, e), 16, c.lo.v[e], 0, 0, 0);
@@ -160,6 +195,7 @@ __device__ __forceinline__ void issue_v_full(const Ctx &c, int s) {
 // missing: halves outside [0, NH) are skipped, rows past skv are clamped to
 // the last key (finite values; their scores are masked). Returns the number
 // of direct loads issued.
+template <bool CAT>
 __device__ __forceinline__ int issue_k_partial(const Ctx &c, int s) {
     const int r = c.lane & 15, g = c.lane >> 4;
     int n_issued = 0;
@@ -171,7 +207,7 @@ __device__ __forceinline__ int issue_k_partial(const Ctx &c, int s) {
         const int half = 2 * s + 1 + u;
         if (half < 0 || half >= c.NH) continue;  // wave-uniform
         const int key = min(32 * half + kperm(kb, r), c.skv - 1);
-        const char *src = c.kh + ((int64_t)key * D + 32 * kk + 8 * g) * 2;
+        const char *src = k_half<CAT>(c, half) + ((int64_t)(key - 32 * half) * D + 32 * kk + 8 * g) * 2;
         __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)frag_dst(c, s, 0, e), 16, 0, 0);
         ++n_issued;
     }
@@ -181,9 +217,9 @@ __device__ __forceinline__ int issue_k_partial(const Ctx &c, int s) {
 // This wave's V^T fragments of stage s through registers: keys past skv are
 // stored as zeros, so the zero probabilities of masked keys never meet
 // non-finite data.
+template <bool CAT>
 __device__ __forceinline__ void stage_v_partial(const Ctx &c, int s) {
     const int r = c.lane & 15, g = c.lane >> 4;
-    const half_t *vh = reinterpret_cast<const half_t *>(c.vh);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 2 * c.wave + e;
@@ -191,7 +227,8 @@ __device__ __forceinline__ void stage_v_partial(const Ctx &c, int s) {
         const int half = 2 * s + u;
         if (half < 0 || half >= c.NH) continue;  // wave-uniform
         const int key = 32 * half + 8 * g;
-        const half_t *src = vh + (int64_t)(16 * mb + r) * c.vrs + key;
+        const half_t *src = reinterpret_cast<const half_t *>(v_half<CAT>(c, half)) + (int64_t)(16 * mb + r) * c.vrs +
+                            8 * g;
         half8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (key + j < c.skv) ? src[j] : (half_t)0.0f;
@@ -201,22 +238,23 @@ __device__ __forceinline__ void stage_v_partial(const Ctx &c, int s) {
 
 // Issue stage s (any position in the key loop); returns the number of direct
 // loads it left in flight (register-path stores complete before returning).
+template <bool CAT>
 __device__ __forceinline__ int issue_stage(const Ctx &c, int s) {
     int n = 0;
     if (2 * s + 1 < c.NH) {  // some K half of the stage exists
         if (s >= 0 && (int64_t)s * BN + 96 <= c.skv) {
-            issue_k_full(c, s);
+            issue_k_full<CAT>(c, s);
             n += 2;
         } else {
-            n += issue_k_partial(c, s);
+            n += issue_k_partial<CAT>(c, s);
         }
     }
     if (s >= 0 && 2 * s < c.NH) {  // some V^T half of the stage exists
         if ((int64_t)(s + 1) * BN <= c.skv) {
-            issue_v_full(c, s);
+            issue_v_full<CAT>(c, s);
             n += 2;
         } else {
-            stage_v_partial(c, s);
+            stage_v_partial<CAT>(c, s);
         }
     }
     return n;
@@ -370,7 +408,7 @@ struct State {
 // fr holds the next RA operands on entry and exit, running on into the next
 // stage, and stage t+3's direct loads go out at fixed points. Otherwise every
 // condition is checked and reads stay within the half.
-template <bool PRE, bool STEADY, int U>
+template <bool PRE, bool CAT, bool STEADY, int U>
 __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &sn, State &st, half8 (&fr)[RA]) {
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
@@ -389,8 +427,8 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
             fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
             // stage t+3's direct loads go out a quarter of the way into each
             // half-step (K, then V^T) rather than in one burst at the step's start
-            if (U == 0 && n == 4) issue_k_full(c, t + 3);
-            if (U == 1 && n == 4) issue_v_full(c, t + 3);
+            if (U == 0 && n == 4) issue_k_full<CAT>(c, t + 3);
+            if (U == 1 && n == 4) issue_v_full<CAT>(c, t + 3);
         } else {
             a = rd(cur + (U * HFRAG + n) * FRAG);
         }
@@ -434,7 +472,7 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
 // the accumulator value -m (four copies of the row's reference, built for
 // that MFMA) instead of 0 -- so the softmax needs no per-score FMA; m_run is
 // then kept in log2 units.
-template <bool PRE>
+template <bool PRE, bool CAT>
 __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -444,17 +482,17 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     const int nqb = (a.sq + BQ - 1) / BQ;
     const int per_split = nqb * a.num_heads;
     // a key split, or one of several K/V blocks (both give a packed partial per part)
-    const int split = (a.n_split > 1 || a.n_kv_blocks > 0) ? work / per_split : 0;
+    const bool blocks = !CAT && a.n_kv_blocks > 0;
+    const int split = (a.n_split > 1 || blocks) ? work / per_split : 0;
     const int head = (work - split * per_split) / nqb;
     const int qb = (work - split * per_split) % nqb;
     const int key_base = a.n_split > 1 ? split * a.split_len : 0;
-    const bool blocks = a.n_kv_blocks > 0;
     const int skv = blocks ? a.kv_len[split] : a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
     const half_t *kbase = blocks ? a.kv_k[split] + (int64_t)head * a.kv_k_head_stride[split]
                                  : a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D;
     const half_t *vbase = blocks ? a.kv_vt[split] + (int64_t)head * a.kv_v_head_stride[split]
                                  : a.vt + (int64_t)head * a.v_head_stride + key_base;
-    const int64_t vrs = blocks ? a.kv_v_row_stride[split] : a.v_row_stride;
+    const int64_t vrs = CAT ? a.kv_v_row_stride[0] : blocks ? a.kv_v_row_stride[split] : a.v_row_stride;
     float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
     float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
     const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
@@ -484,21 +522,25 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     c.vh = reinterpret_cast<const char *>(vbase);
     c.ring = smem;
     c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
-    c.lo = load_offsets(vrs, wave, lane);
+    c.lo = load_offsets(vrs, wave, lane, CAT);
     c.wave = wave;
     c.lane = lane;
     c.skv = skv;
     c.NH = (skv + 31) / 32;
     c.T = (skv + BN - 1) / BN;
     c.vrs = vrs;
+    c.a = &a;
+    c.head = head;
+    c.key_base = key_base;
+    c.lg_len = a.kv_lg_len;
     const int T = c.T;
 
     if (T > 0) {
         SBlk sa, sb;
-        issue_stage(c, -1);
-        issue_stage(c, 0);
-        issue_stage(c, 1);
-        wait_vm_lgkm(issue_stage(c, 2));  // stages -1, 0, 1 complete
+        issue_stage<CAT>(c, -1);
+        issue_stage<CAT>(c, 0);
+        issue_stage<CAT>(c, 1);
+        wait_vm_lgkm(issue_stage<CAT>(c, 2));  // stages -1, 0, 1 complete
         barrier_no_fence();
         {
             // S of key half 0 from stage -1's second K half (slot 3)
@@ -540,16 +582,16 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
 #pragma unroll
             for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
             for (; t < n_steady; ++t) {
-                half_step<PRE, true, 0>(c, t, sa, sb, st, fr);
-                half_step<PRE, true, 1>(c, t, sb, sa, st, fr);
+                half_step<PRE, CAT, true, 0>(c, t, sa, sb, st, fr);
+                half_step<PRE, CAT, true, 1>(c, t, sb, sa, st, fr);
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
                 barrier_no_fence();
             }
         }
         for (; t < T; ++t) {
-            const int inflight = issue_stage(c, t + 3);
-            half_step<PRE, false, 0>(c, t, sa, sb, st, fr);
-            half_step<PRE, false, 1>(c, t, sb, sa, st, fr);
+            const int inflight = issue_stage<CAT>(c, t + 3);
+            half_step<PRE, CAT, false, 0>(c, t, sa, sb, st, fr);
+            half_step<PRE, CAT, false, 1>(c, t, sb, sa, st, fr);
             if (t + 1 < T) {
                 wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
                 barrier_no_fence();
@@ -635,10 +677,10 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
 // One workgroup per (key split, head, 384-row query block) item, remapped so
 // each XCD works through a contiguous range of items and its concurrent
 // workgroups share one head's K/V in L2.
-template <bool PRE>
+template <bool PRE, bool CAT>
 __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
-    attend_item<PRE>(a, xcd_remap(blockIdx.x, gridDim.x), smem);
+    attend_item<PRE, CAT>(a, xcd_remap(blockIdx.x, gridDim.x), smem);
 }
 
 }  // namespace
@@ -646,12 +688,17 @@ __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
 hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     if (a.sq <= 0) return hipSuccess;
     const int nqb = (a.sq + BQ - 1) / BQ;
-    const int parts = a.n_kv_blocks > 0 ? a.n_kv_blocks : a.n_split > 1 ? a.n_split : 1;
+    const int parts = (a.n_kv_blocks > 0 && !a.kv_concat) ? a.n_kv_blocks : a.n_split > 1 ? a.n_split : 1;
     const int blocks = nqb * a.num_heads * parts;
-    if (a.q_log2e)
-        hipLaunchKernelGGL(flash_fwd_f16_d128<true>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
-    else
-        hipLaunchKernelGGL(flash_fwd_f16_d128<false>, dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    if (a.kv_concat) {
+        // keys in equal blocks read as one sequence: q_scaled from the caller
+        if (a.q_log2e || a.n_kv_blocks <= 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((flash_fwd_f16_d128<false, true>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    } else if (a.q_log2e) {
+        hipLaunchKernelGGL((flash_fwd_f16_d128<true, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((flash_fwd_f16_d128<false, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -733,7 +780,8 @@ AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems)
 
 hipError_t launch_attention_f16(const FlashArgs &a, const AttnPlan &p, float *ws_o, float *ws_lse,
                                 hipStream_t stream) {
-    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || a.n_kv_blocks > 0 || (a.o16 && a.o32) ||
+    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || (a.n_kv_blocks > 0 && !a.kv_concat) ||
+        (a.o16 && a.o32) ||
         (!a.o16 && !a.o32) || !ws_o || !ws_lse)
         return launch_flash_fwd_f16(a, stream);
     hipError_t e = hipSuccess;

@@ -50,6 +50,12 @@ struct FlashArgs {
     const _Float16 *kv_vt[kMaxKvBlocks];
     int64_t kv_k_head_stride[kMaxKvBlocks], kv_v_head_stride[kMaxKvBlocks], kv_v_row_stride[kMaxKvBlocks];
     int kv_len[kMaxKvBlocks];
+    // Non-zero (with n_kv_blocks > 0, q_log2e 0): the blocks are one key
+    // sequence of skv keys, block b holding keys [b << kv_lg_len, ...); every
+    // block but the last has 2^kv_lg_len >= 64 keys, and all share one V^T row
+    // stride. The launch is then an ordinary attention over those keys
+    // (outputs as without blocks; n_split splits that sequence).
+    int kv_concat, kv_lg_len;
 };
 
 struct FlashArgsF32 {

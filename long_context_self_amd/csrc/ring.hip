@@ -160,6 +160,40 @@ ATTN_API attn_status_t attn_ring_forward(attn_ring_t *ring, const void *q_scaled
     for (int b = 0; b < nb && all_resident; ++b)
         all_resident = block_lens[b] == 0 || (on_device(k_blocks[b], ring->device) &&
                                               on_device(vt_blocks[b], ring->device));
+    // Equal blocks of a power-of-two length: they are one key sequence, so the
+    // launch is an ordinary planned attention over all nb * len keys with no
+    // per-block partials and no merge of them.
+    int lg = 0;
+    bool equal_pow2 = all_resident && block_lens[0] >= 64 && (block_lens[0] & (block_lens[0] - 1)) == 0;
+    for (int b = 1; b < nb && equal_pow2; ++b) equal_pow2 = block_lens[b] == block_lens[0];
+    if (equal_pow2) {
+        while ((int64_t(1) << lg) < block_lens[0]) ++lg;
+        const int64_t len = block_lens[0], ld = ATTN_VT_LD(len);
+        FlashArgs fa{};
+        fa.q = static_cast<const _Float16 *>(q_scaled);
+        fa.q_head_stride = sq * d;
+        fa.sq = (int)sq;
+        fa.skv = (int)(nb * len);
+        fa.num_heads = H;
+        fa.o16 = static_cast<_Float16 *>(o_out);
+        fa.o16_ld = (int64_t)H * d;
+        fa.lse = lse_out;
+        fa.n_kv_blocks = nb;
+        fa.kv_concat = 1;
+        fa.kv_lg_len = lg;
+        for (int b = 0; b < nb; ++b) {
+            fa.kv_k[b] = static_cast<const _Float16 *>(k_blocks[b]);
+            fa.kv_vt[b] = static_cast<const _Float16 *>(vt_blocks[b]);
+            fa.kv_k_head_stride[b] = len * d;
+            fa.kv_v_head_stride[b] = (int64_t)d * ld;
+            fa.kv_v_row_stride[b] = ld;
+            fa.kv_len[b] = (int)len;
+        }
+        const AttnPlan plan = plan_attention_f16(H, (int)sq, fa.skv, kPartialWsFloats);
+        HIP_TRY("attn_ring_forward: attention",
+                launch_attention_f16(fa, plan, ring->split_ws, ring->split_ws + plan.o_elems, stream));
+        return ATTN_OK;
+    }
     if (all_resident) {
         FlashArgs fa{};
         fa.q = static_cast<const _Float16 *>(q_scaled);

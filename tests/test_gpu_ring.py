@@ -141,6 +141,37 @@ def test_ring_device_resident_blocks_one_launch():
     assert torch.equal(o, o3) and torch.equal(lse, lse3), "one-launch ring not deterministic"
 
 
+def test_ring_equal_device_blocks_read_as_one_sequence():
+    # Equal power-of-two blocks in device memory: the ring reads them as one key
+    # sequence in a single planned launch (no per-block partials), which equals
+    # attn_partial_forward_vt over the concatenated K/V bit for bit (after the
+    # same fp16 rounding), and meets the oracle's gates.
+    hh, sq, d = 8, 700, 128
+    lens = [1024] * 4
+    say(f"ring, equal device-resident blocks {lens}, H={hh} sq={sq}")
+    q, k, v = attention_inputs(hh, sq, sum(lens), d, seed=46)
+    kb, vb = _blocks(k, v, lens)
+    qd = dev(q)
+    o, lse = _ring(qd, sq, kb, vb, lens, hh, d)
+    o_ref, lse_ref = oracle.partial_attention(q[:2], k[:2], v[:2])
+    got = host(o).reshape(sq, hh, d).transpose(1, 0, 2)
+    assert_close(got[:2], o_ref, what="ring O (one sequence)")
+    assert_close(host(lse)[:2], lse_ref, what="ring LSE (one sequence)")
+    skv = sum(lens)
+    ld = B.vt_ld(skv)
+    vt = np.zeros((hh, d, ld), dtype=np.float16)
+    vt[:, :, :skv] = v.transpose(0, 2, 1)
+    o32 = torch.empty((hh, sq, d), dtype=torch.float32, device="cuda")
+    l32 = torch.empty((hh, sq), dtype=torch.float32, device="cuda")
+    B.attn_partial_forward_vt(hh, d, qd, sq, sq * d, dev(k), skv, skv * d, dev(vt), d * ld, ld, o32, l32)
+    torch.cuda.synchronize()
+    o_cat = o32.transpose(0, 1).reshape(sq, hh * d).to(torch.float16)
+    assert torch.equal(o, o_cat) and torch.equal(lse, l32), "ring differs from one partial over the concatenated keys"
+    o2, lse2 = _sequential(qd, sq, kb, vb, lens, hh, d)
+    assert rel_l2(host(o).astype(np.float64), host(o2).astype(np.float64)) <= REL_L2_SPLIT
+    assert rel_l2(host(lse), host(lse2)) <= REL_L2_SPLIT
+
+
 def test_ring_config_seq32768_rank0_pinned():
     seq, h, nh, ranks = 32768, 4096, 32, 8
     d, ch = h // nh, seq // ranks
