@@ -24,10 +24,11 @@
 //   hold 8 consecutive keys of its own query; after exp and a cast those are
 //   the B operand of the PV product, with no data movement between lanes.
 // * Software pipeline per wave: each half-step issues the MFMAs of the next
-//   32 keys' scores and of O += V P for the current 32 keys, and computes
-//   exp(S) -> P before the PV MFMAs that need it, then the row sums of P and
-//   the row maxima of the next scores, so the softmax VALU work shares the
-//   wave's instruction stream with its own matrix work.
+//   32 keys' scores and of O += V P for the current 32 keys (P computed by the
+//   half-step before). Beside them it adds up the current P, and once the
+//   scores are in, computes their P and checks them against the reference
+//   max, so the softmax VALU work shares the wave's instruction stream with
+//   its own matrix work and one score buffer serves every half-step.
 // * K/V^T reach LDS by direct global->LDS loads (no staging registers) into a
 //   4-slot ring, issued three stages ahead. LDS holds every tile in MFMA
 //   operand order: fragment n of a stage is 64 lanes x 16 bytes, so every
@@ -352,12 +353,13 @@ __device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, flo
 // reference says nothing about the rest of its row, so the row maxima (a
 // reduction over four lanes) are formed only when some lane of the wave is
 // over; otherwise every score of the wave is within 2^8 and nothing changes.
-__device__ __forceinline__ void update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+__device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
                                            floatx4 (&o)[8][NQ]) {
     bool over = false;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) over = over || lm[j] > m_run[j] + kRescaleTau;
-    if (__ballot(over)) {
+    if (!__ballot(over)) return false;
+    {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const float mt = max_over_key_lanes(lm[j]);
@@ -369,18 +371,20 @@ __device__ __forceinline__ void update_max(const float (&lm)[NQ], float (&m_run)
             for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
         }
     }
+    return true;
 }
 
 // The same for PRE scores, which are relative to the reference already
 // (log2 units): the row max mt of S - m. Where it exceeds 8 the reference
 // moves up by mt, and O, the sum and the pending scores follow it (later
 // halves start their S accumulators from the new -m).
-__device__ __forceinline__ void update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
-                                               floatx4 (&o)[8][NQ], SBlk &s) {
+__device__ __forceinline__ bool update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+                                               floatx4 (&o)[8][NQ], SBlk &s, floatx4 (&negm)[NQ]) {
     bool over = false;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) over = over || lm[j] > 8.0f;
-    if (__ballot(over)) {
+    if (!__ballot(over)) return false;
+    {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const float mt = max_over_key_lanes(lm[j]);
@@ -392,31 +396,34 @@ __device__ __forceinline__ void update_max_rel(const float (&lm)[NQ], float (&m_
             for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) s[kb][j] -= delta;
+            negm[j] = splat4(-m_run[j]);
         }
     }
+    return true;
 }
 
 struct State {
     floatx4 o[8][NQ];  // O^T accumulators [head-dim block][query block]
     half8 qf[NQ][4];   // Q as B operands [query block][head-dim step]
+    floatx4 negm[NQ];  // PRE: -m, the start value of each S accumulation chain
     float m_run[NQ], l_run[NQ];
 };
 
-// Half U of step t: P of key half 2t+U from sc, O += V P over it, and the
-// scores of key half 2t+U+1 into sn (their row maxima folded into the
-// reference). STEADY: every half this step touches and stage t+3 are full;
+// Half U of step t: O += V P over key half 2t+U (pf, from the half-step
+// before), the scores of key half 2t+U+1 into sc, and their P into pf (after
+// the rescale check, redone if the reference moved). STEADY: every half this
+// step touches and stage t+3 are full;
 // fr holds the next RA operands on entry and exit, running on into the next
 // stage, and stage t+3's direct loads go out at fixed points. Otherwise every
 // condition is checked and reads stay within the half.
 template <bool PRE, bool CAT, bool STEADY, int U>
-__device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &sn, State &st, half8 (&fr)[RA]) {
+__device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (&pf)[NQ], State &st,
+                                          half8 (&fr)[RA]) {
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
     const int hv = 2 * t + U;  // key half of this PV
     const bool has_pv = STEADY || hv < c.NH;
     const bool has_s = STEADY || hv + 1 < c.NH;
-    half8 pf[NQ];
-    if (has_pv) exp_and_pack<PRE>(sc, pf, st.m_run);
 #pragma unroll
     for (int n = 0; n < HFRAG; ++n) {
         if (!(n < 8 ? has_s : has_pv)) continue;  // wave-uniform
@@ -436,7 +443,7 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
             const int kk = n >> 1, kb = n & 1;
 #pragma unroll
             for (int j = 0; j < NQ; ++j)
-                sn[kb][j] = mfma16(a, st.qf[j][kk], kk == 0 ? (PRE ? splat4(-st.m_run[j]) : floatx4{}) : sn[kb][j]);
+                sc[kb][j] = mfma16(a, st.qf[j][kk], kk == 0 ? (PRE ? st.negm[j] : floatx4{}) : sc[kb][j]);
         } else {
             const int mb = n - 8;
 #pragma unroll
@@ -448,13 +455,18 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
         float lm[NQ];
         const int g = c.lane >> 4;
         if (STEADY || 32 * (hv + 2) <= c.skv)
-            local_max<false>(sn, hv + 1, c.skv, g, lm);
+            local_max<false>(sc, hv + 1, c.skv, g, lm);
         else
-            local_max<true>(sn, hv + 1, c.skv, g, lm);
-        if (PRE)
-            update_max_rel(lm, st.m_run, st.l_run, st.o, sn);
-        else
-            update_max(lm, st.m_run, st.l_run, st.o);
+            local_max<true>(sc, hv + 1, c.skv, g, lm);
+        // P of the next half against the current reference, before the check:
+        // redone only when the check moves the reference
+        exp_and_pack<PRE>(sc, pf, st.m_run);
+        // keep that work ahead of the branch (in the block with the MFMAs),
+        // where the compiler would otherwise sink it into the no-rescale path
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
+        const bool moved = PRE ? update_max_rel(lm, st.m_run, st.l_run, st.o, sc, st.negm)
+                               : update_max(lm, st.m_run, st.l_run, st.o);
+        if (moved) exp_and_pack<PRE>(sc, pf, st.m_run);
     }
 }
 
@@ -469,9 +481,9 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, SBlk &s
 // PRE (set when q holds q_scaled * log2(e), as the block's projection writes
 // it): the scores come out of the S MFMAs already as (S - m) log2(e) -- the
 // log2(e) factor rides in Q and the first MFMA of each S chain starts from
-// the accumulator value -m (four copies of the row's reference, built for
-// that MFMA) instead of 0 -- so the softmax needs no per-score FMA; m_run is
-// then kept in log2 units.
+// the accumulator value -m (negm, four copies of the row's reference) instead
+// of 0 -- so the softmax needs no per-score FMA; m_run is then kept in log2
+// units.
 template <bool PRE, bool CAT>
 __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
     const int tid = threadIdx.x;
@@ -536,7 +548,8 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     const int T = c.T;
 
     if (T > 0) {
-        SBlk sa, sb;
+        SBlk sa;
+        half8 pf[NQ];
         issue_stage<CAT>(c, -1);
         issue_stage<CAT>(c, 0);
         issue_stage<CAT>(c, 1);
@@ -566,10 +579,12 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
                 st.m_run[j] = mt;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) sa[kb][j] -= mt;
+                st.negm[j] = splat4(-mt);
             }
         } else {
             update_max(lm, st.m_run, st.l_run, st.o);
         }
+        exp_and_pack<PRE>(sa, pf, st.m_run);
         // Step 0 refills slot 3: every wave must be done reading it.
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
         barrier_no_fence();
@@ -582,16 +597,16 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
 #pragma unroll
             for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
             for (; t < n_steady; ++t) {
-                half_step<PRE, CAT, true, 0>(c, t, sa, sb, st, fr);
-                half_step<PRE, CAT, true, 1>(c, t, sb, sa, st, fr);
+                half_step<PRE, CAT, true, 0>(c, t, sa, pf, st, fr);
+                half_step<PRE, CAT, true, 1>(c, t, sa, pf, st, fr);
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
                 barrier_no_fence();
             }
         }
         for (; t < T; ++t) {
             const int inflight = issue_stage<CAT>(c, t + 3);
-            half_step<PRE, CAT, false, 0>(c, t, sa, sb, st, fr);
-            half_step<PRE, CAT, false, 1>(c, t, sb, sa, st, fr);
+            half_step<PRE, CAT, false, 0>(c, t, sa, pf, st, fr);
+            half_step<PRE, CAT, false, 1>(c, t, sa, pf, st, fr);
             if (t + 1 < T) {
                 wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
                 barrier_no_fence();
