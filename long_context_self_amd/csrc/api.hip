@@ -388,7 +388,7 @@ ATTN_API attn_status_t attn_heads_forward(int num_heads, int head_dim, attn_dtyp
         fa.lse = lse;
         const AttnPlan plan = plan_attention_f16(num_heads, (int)seq, (int)seq, kSplitWsFloats);
         if (plan.n_split <= 1) {
-            HIP_TRY("attn_heads_forward", launch_flash_fwd_f16(fa, stream));
+            HIP_TRY("attn_heads_forward", launch_attention_f16(fa, plan, nullptr, nullptr, stream));
             return ATTN_OK;
         }
         hipMemPool_t pool = nullptr;

@@ -54,10 +54,9 @@ namespace attnblk {
 namespace {
 
 constexpr int D = 128;       // head_dim
-constexpr int NQ = 3;        // 16-row query blocks per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int BQ = NWAVES * 16 * NQ;  // query rows per workgroup (384)
+constexpr int kMaxNQ = 3;             // 16-row query blocks per wave: 3 (384-row workgroups) or 2 (256)
 constexpr int BN = 64;                // keys per stage
 constexpr int FRAG = 64 * 8;          // halves in one MFMA operand fragment
 constexpr int HFRAG = 16;             // fragments per half-stage: 8 of K, then 8 of V^T
@@ -66,7 +65,7 @@ constexpr int RING_BYTES = 4 * SLOT * 2;  // stage s lives in slot s % 4
 constexpr int RA = 2;                     // operand reads in flight ahead of the MFMAs
 constexpr int OP16 = D + 8;               // O staging pitch, fp16 (halves)
 constexpr int OP32 = D + 4;               // O staging pitch, fp32 (floats)
-constexpr int OSTAGE16 = NWAVES * 16 * NQ * OP16 * 2;
+constexpr int OSTAGE16 = NWAVES * 16 * kMaxNQ * OP16 * 2;
 constexpr int OSTAGE32 = NWAVES * 16 * OP32 * 4;
 constexpr int SMEM_BYTES = RING_BYTES;
 static_assert(OSTAGE16 <= RING_BYTES && OSTAGE32 <= RING_BYTES, "O staging reuses the ring");
@@ -278,6 +277,12 @@ __device__ __forceinline__ void wait_vm_lgkm(int n) {
 
 __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<const half8 *>(p); }
 
+// Everything that depends on the number NQ of 16-row query blocks per wave:
+// three (384-row workgroups, the default) or two (256 rows, for grids that
+// fill the CUs better in smaller pieces). Per-row arithmetic is the same.
+template <int NQ>
+struct Rows {
+static constexpr int BQ = NWAVES * 16 * NQ;  // query rows per workgroup
 typedef floatx4 SBlk[2][NQ];  // scores of one 32-key half: [key block][query block]
 
 // P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
@@ -286,7 +291,7 @@ typedef floatx4 SBlk[2][NQ];  // scores of one 32-key half: [key block][query bl
 // factor and the first S MFMA starts from -m (see the kernel) -- so P is one
 // exp2 per score; otherwise one FMA per score maps S to that argument.
 template <bool PRE>
-__device__ __forceinline__ void exp_and_pack(const SBlk &sc, half8 (&pf)[NQ], const float (&m_run)[NQ]) {
+static __device__ __forceinline__ void exp_and_pack(const SBlk &sc, half8 (&pf)[NQ], const float (&m_run)[NQ]) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         const float mneg = -m_run[j] * kLog2e;
@@ -303,7 +308,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // Add the fp16 probabilities (the very values the PV product weights) to the
 // lane's running sums, two per dot instruction with fp32 accumulation.
-__device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_run)[NQ]) {
+static __device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_run)[NQ]) {
     const half2v one = {(half_t)1.0f, (half_t)1.0f};
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
@@ -316,7 +321,7 @@ __device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_ru
 // query's keys). v_permlane16_swap trades the odd 16-lane rows of one
 // register with the even rows of the other; applied to two copies of v it
 // yields v of lane i and of lane i ^ 16 in every lane i.
-__device__ __forceinline__ float max_over_key_lanes(float v) {
+static __device__ __forceinline__ float max_over_key_lanes(float v) {
     v = wave_max_across_halves(v);
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -326,7 +331,7 @@ __device__ __forceinline__ float max_over_key_lanes(float v) {
 // half `half`, masking keys past skv. The row maximum is that over the four
 // lanes of the query (max_over_key_lanes).
 template <bool MASK>
-__device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, float (&lm)[NQ]) {
+static __device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, float (&lm)[NQ]) {
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -353,7 +358,7 @@ __device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, flo
 // reference says nothing about the rest of its row, so the row maxima (a
 // reduction over four lanes) are formed only when some lane of the wave is
 // over; otherwise every score of the wave is within 2^8 and nothing changes.
-__device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+static __device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
                                            floatx4 (&o)[8][NQ]) {
     bool over = false;
 #pragma unroll
@@ -378,7 +383,7 @@ __device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)
 // (log2 units): the row max mt of S - m. Where it exceeds 8 the reference
 // moves up by mt, and O, the sum and the pending scores follow it (later
 // halves start their S accumulators from the new -m).
-__device__ __forceinline__ bool update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+static __device__ __forceinline__ bool update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
                                                floatx4 (&o)[8][NQ], SBlk &s, floatx4 (&negm)[NQ]) {
     bool over = false;
 #pragma unroll
@@ -417,7 +422,7 @@ struct State {
 // stage, and stage t+3's direct loads go out at fixed points. Otherwise every
 // condition is checked and reads stay within the half.
 template <bool PRE, bool CAT, bool STEADY, int U>
-__device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (&pf)[NQ], State &st,
+static __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (&pf)[NQ], State &st,
                                           half8 (&fr)[RA]) {
     const half_t *cur = c.rl + (t & 3) * SLOT;
     const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
@@ -485,7 +490,7 @@ __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (
 // of 0 -- so the softmax needs no per-score FMA; m_run is then kept in log2
 // units.
 template <bool PRE, bool CAT>
-__device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
+static __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -689,31 +694,43 @@ __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *
     }
 }
 
-// One workgroup per (key split, head, 384-row query block) item, remapped so
-// each XCD works through a contiguous range of items and its concurrent
+};  // struct Rows
+
+// One workgroup per (key split, head, 128 NQ-row query block) item, remapped
+// so each XCD works through a contiguous range of items and its concurrent
 // workgroups share one head's K/V in L2.
-template <bool PRE, bool CAT>
+template <int NQ, bool PRE, bool CAT>
 __global__ __launch_bounds__(NTHREADS) void flash_fwd_f16_d128(FlashArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
-    attend_item<PRE, CAT>(a, xcd_remap(blockIdx.x, gridDim.x), smem);
+    Rows<NQ>::template attend_item<PRE, CAT>(a, xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+template <int NQ>
+void launch_rows(const FlashArgs &a, int blocks, hipStream_t stream) {
+    if (a.kv_concat)
+        hipLaunchKernelGGL((flash_fwd_f16_d128<NQ, false, true>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    else if (a.q_log2e)
+        hipLaunchKernelGGL((flash_fwd_f16_d128<NQ, true, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((flash_fwd_f16_d128<NQ, false, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
 }
 
 }  // namespace
 
 hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
     if (a.sq <= 0) return hipSuccess;
-    const int nqb = (a.sq + BQ - 1) / BQ;
+    const int nq = a.nq ? a.nq : kMaxNQ;
+    if (nq != 2 && nq != 3) return hipErrorInvalidValue;
+    // keys in equal blocks read as one sequence: q_scaled from the caller
+    if (a.kv_concat && (a.q_log2e || a.n_kv_blocks <= 0)) return hipErrorInvalidValue;
+    const int bq = NWAVES * 16 * nq;
+    const int nqb = (a.sq + bq - 1) / bq;
     const int parts = (a.n_kv_blocks > 0 && !a.kv_concat) ? a.n_kv_blocks : a.n_split > 1 ? a.n_split : 1;
     const int blocks = nqb * a.num_heads * parts;
-    if (a.kv_concat) {
-        // keys in equal blocks read as one sequence: q_scaled from the caller
-        if (a.q_log2e || a.n_kv_blocks <= 0) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((flash_fwd_f16_d128<false, true>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
-    } else if (a.q_log2e) {
-        hipLaunchKernelGGL((flash_fwd_f16_d128<true, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL((flash_fwd_f16_d128<false, false>), dim3(blocks), dim3(NTHREADS), 0, stream, a);
-    }
+    if (nq == 3)
+        launch_rows<3>(a, blocks, stream);
+    else
+        launch_rows<2>(a, blocks, stream);
     return hipGetLastError();
 }
 
@@ -728,6 +745,9 @@ constexpr int kMinSplitKeys = 512;    // shortest key range worth a workgroup
 // once and read once by the merge at about kMergeBw; the two extra launches
 // cost kExtraLaunch.
 constexpr double kItemPerKey = 3.95e-8, kItemFixed = 8e-6, kMergeBw = 4.0e12, kExtraLaunch = 1.5e-5;
+// A 256-row workgroup's time per key relative to a 384-row one (it moves more
+// LDS bytes per product: measured 0.71 at seq 65536, 0.75 at 8192).
+constexpr double kRows256Cost = 0.75;
 
 std::atomic<int> g_cus[kMaxDevices];
 
@@ -761,43 +781,53 @@ int cu_count() {
 // counting the merge traffic and the extra launches, and no split unless
 // that gains at least 1% over the plain launch.
 AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems) {
-    AttnPlan p{sq, 1, 0, 0, 0};
-    if (num_heads <= 0 || sq <= 0 || skv < 2 * kMinSplitKeys) return p;
+    AttnPlan p{sq, 1, 0, 0, 0, kMaxNQ};
+    if (num_heads <= 0 || sq <= 0 || skv <= 0) return p;
     const int64_t C = cu_count();
-    const int nqb = (sq + BQ - 1) / BQ;
-    const double t_item = kItemPerKey * skv + kItemFixed;
     auto rounds = [C](int64_t n) { return (double)((n + C - 1) / C); };
-    const double plain = rounds((int64_t)nqb * num_heads) * t_item;
-    double best = 0.99 * plain;
-    const int tb_max = (int)std::min<int64_t>(nqb, 2 * C / num_heads + 1);
-    for (int tb = 1; tb <= nqb; ++tb) {
-        if (tb > tb_max && tb != nqb) continue;
-        const int main_rows = (nqb - tb) * BQ;
-        const int tail_rows = sq - main_rows;
-        for (int k = 2; k <= kMaxSplit; ++k) {
-            const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
-            if (len < kMinSplitKeys) break;
-            const int ke = (skv + len - 1) / len;
-            const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
-            if (o_el > max_o_elems) break;
-            const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
-            const double t = rounds((int64_t)(nqb - tb) * num_heads) * t_item +
-                             rounds((int64_t)tb * num_heads * ke) * (kItemPerKey * len + kItemFixed) + merge +
-                             kExtraLaunch;
-            if (t < best) {
-                best = t;
-                p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows};
+    // the plain launch of 384-row workgroups is what any other plan must beat by 1%
+    double best = 0.99 * rounds((int64_t)((sq + 383) / 384) * num_heads) * (kItemPerKey * skv + kItemFixed);
+    for (int nq = kMaxNQ; nq >= 2; --nq) {
+        const int bq = NWAVES * 16 * nq;
+        const double per_key = kItemPerKey * (nq == kMaxNQ ? 1.0 : kRows256Cost);
+        const int nqb = (sq + bq - 1) / bq;
+        const double t_item = per_key * skv + kItemFixed;
+        if (nq != kMaxNQ && rounds((int64_t)nqb * num_heads) * t_item < best) {
+            best = rounds((int64_t)nqb * num_heads) * t_item;
+            p = AttnPlan{sq, 1, 0, 0, 0, nq};
+        }
+        if (skv < 2 * kMinSplitKeys) continue;
+        const int tb_max = (int)std::min<int64_t>(nqb, 2 * C / num_heads + 1);
+        for (int tb = 1; tb <= nqb; ++tb) {
+            if (tb > tb_max && tb != nqb) continue;
+            const int main_rows = (nqb - tb) * bq;
+            const int tail_rows = sq - main_rows;
+            for (int k = 2; k <= kMaxSplit; ++k) {
+                const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
+                if (len < kMinSplitKeys) break;
+                const int ke = (skv + len - 1) / len;
+                const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
+                if (o_el > max_o_elems) break;
+                const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
+                const double t = rounds((int64_t)(nqb - tb) * num_heads) * t_item +
+                                 rounds((int64_t)tb * num_heads * ke) * (per_key * len + kItemFixed) + merge +
+                                 kExtraLaunch;
+                if (t < best) {
+                    best = t;
+                    p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows, nq};
+                }
             }
         }
     }
     return p;
 }
 
-hipError_t launch_attention_f16(const FlashArgs &a, const AttnPlan &p, float *ws_o, float *ws_lse,
+hipError_t launch_attention_f16(const FlashArgs &args, const AttnPlan &p, float *ws_o, float *ws_lse,
                                 hipStream_t stream) {
+    FlashArgs a = args;
+    a.nq = p.nq;
     if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || (a.n_kv_blocks > 0 && !a.kv_concat) ||
-        (a.o16 && a.o32) ||
-        (!a.o16 && !a.o32) || !ws_o || !ws_lse)
+        (a.o16 && a.o32) || (!a.o16 && !a.o32) || !ws_o || !ws_lse)
         return launch_flash_fwd_f16(a, stream);
     hipError_t e = hipSuccess;
     const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;

@@ -56,6 +56,8 @@ struct FlashArgs {
     // stride. The launch is then an ordinary attention over those keys
     // (outputs as without blocks; n_split splits that sequence).
     int kv_concat, kv_lg_len;
+    // 16-row query blocks per wave: 3 (384-row workgroups; also 0) or 2 (256).
+    int nq;
 };
 
 struct FlashArgsF32 {
@@ -148,10 +150,12 @@ struct MergeArgs {
 // [0, main_rows) of every head run as whole-key workgroups; the rows
 // [main_rows, sq) run split into n_split key ranges of split_len keys, whose
 // fp32 partials (o_elems and lse_elems floats of workspace) are then merged
-// into the outputs. n_split <= 1: one plain launch.
+// into the outputs. n_split <= 1: one plain launch. nq: 16-row query blocks
+// per wave of every launch (3: 384-row workgroups; 2: 256).
 struct AttnPlan {
     int main_rows, n_split, split_len;
     int64_t o_elems, lse_elems;
+    int nq;
 };
 
 // Workspace budgets of a key-split attention tail (floats of partial rows):

@@ -94,7 +94,7 @@ attn_status_t enqueue_partial(const char *what, int num_heads, int head_dim, int
         fa.lse = lse_part;
         const AttnPlan plan = plan_attention_f16(num_heads, (int)sq, (int)skv, kPartialWsFloats);
         if (plan.n_split <= 1) {
-            HIP_TRY(what, launch_flash_fwd_f16(fa, stream));
+            HIP_TRY(what, launch_attention_f16(fa, plan, nullptr, nullptr, stream));
             return ATTN_OK;
         }
         void *pooled = nullptr;
