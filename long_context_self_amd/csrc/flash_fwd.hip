@@ -282,417 +282,417 @@ __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<
 // fill the CUs better in smaller pieces). Per-row arithmetic is the same.
 template <int NQ>
 struct Rows {
-static constexpr int BQ = NWAVES * 16 * NQ;  // query rows per workgroup
-typedef floatx4 SBlk[2][NQ];  // scores of one 32-key half: [key block][query block]
+    static constexpr int BQ = NWAVES * 16 * NQ;  // query rows per workgroup
+    typedef floatx4 SBlk[2][NQ];  // scores of one 32-key half: [key block][query block]
 
-// P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
-// pf[j] holds keys 8(l / 16) + 0..7 of the lane's query in block j.
-// PRE: the scores are already (S - m) log2(e) -- Q carries the log2(e)
-// factor and the first S MFMA starts from -m (see the kernel) -- so P is one
-// exp2 per score; otherwise one FMA per score maps S to that argument.
-template <bool PRE>
-static __device__ __forceinline__ void exp_and_pack(const SBlk &sc, half8 (&pf)[NQ], const float (&m_run)[NQ]) {
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        const float mneg = -m_run[j] * kLog2e;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                pf[j][4 * kb + r] =
-                    (half_t)__builtin_amdgcn_exp2f(PRE ? sc[kb][j][r] : fmaf(sc[kb][j][r], kLog2e, mneg));
-    }
-}
-
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
-// Add the fp16 probabilities (the very values the PV product weights) to the
-// lane's running sums, two per dot instruction with fp32 accumulation.
-static __device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_run)[NQ]) {
-    const half2v one = {(half_t)1.0f, (half_t)1.0f};
-#pragma unroll
-    for (int j = 0; j < NQ; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2)
-            l_run[j] = __builtin_amdgcn_fdot2(half2v{pf[j][i], pf[j][i + 1]}, one, l_run[j], false);
-}
-
-// max(v) over lanes i, i ^ 16, i ^ 32, i ^ 48 (the four lanes that hold one
-// query's keys). v_permlane16_swap trades the odd 16-lane rows of one
-// register with the even rows of the other; applied to two copies of v it
-// yields v of lane i and of lane i ^ 16 in every lane i.
-static __device__ __forceinline__ float max_over_key_lanes(float v) {
-    v = wave_max_across_halves(v);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Each lane's maximum over its own 8 scores of every query block, for key
-// half `half`, masking keys past skv. The row maximum is that over the four
-// lanes of the query (max_over_key_lanes).
-template <bool MASK>
-static __device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, float (&lm)[NQ]) {
-    if (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool out = 32 * half + 8 * g + 4 * kb + r >= skv;
-#pragma unroll
-                for (int j = 0; j < NQ; ++j)
-                    if (out) s[kb][j][r] = -INFINITY;
-            }
-    }
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        // three-operand max chains: four instructions for eight values
-        const float a = fmaxf(fmaxf(s[0][j][0], s[0][j][1]), s[0][j][2]);
-        const float b = fmaxf(fmaxf(s[0][j][3], s[1][j][0]), s[1][j][1]);
-        lm[j] = fmaxf(fmaxf(fmaxf(a, b), s[1][j][2]), s[1][j][3]);
-    }
-}
-
-// Given the lanes' local maxima lm of the next scores: where some row's max
-// grew by more than 2^8, raise its reference to the new row max and rescale O
-// and the running sum to it. A lane whose own scores stay within 2^8 of the
-// reference says nothing about the rest of its row, so the row maxima (a
-// reduction over four lanes) are formed only when some lane of the wave is
-// over; otherwise every score of the wave is within 2^8 and nothing changes.
-static __device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
-                                           floatx4 (&o)[8][NQ]) {
-    bool over = false;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) over = over || lm[j] > m_run[j] + kRescaleTau;
-    if (!__ballot(over)) return false;
-    {
-#pragma unroll
+    // P = exp(S - m) (exp2 domain) as the fp16 B operands of the PV product:
+    // pf[j] holds keys 8(l / 16) + 0..7 of the lane's query in block j.
+    // PRE: the scores are already (S - m) log2(e) -- Q carries the log2(e)
+    // factor and the first S MFMA starts from -m (see the kernel) -- so P is one
+    // exp2 per score; otherwise one FMA per score maps S to that argument.
+    template <bool PRE>
+    static __device__ __forceinline__ void exp_and_pack(const SBlk &sc, half8 (&pf)[NQ], const float (&m_run)[NQ]) {
+    #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            const float mt = max_over_key_lanes(lm[j]);
-            const float m_new = mt > m_run[j] + kRescaleTau ? mt : m_run[j];
-            const float alpha = __builtin_amdgcn_exp2f((m_run[j] - m_new) * kLog2e);
-            m_run[j] = m_new;
-            l_run[j] *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
+            const float mneg = -m_run[j] * kLog2e;
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pf[j][4 * kb + r] =
+                        (half_t)__builtin_amdgcn_exp2f(PRE ? sc[kb][j][r] : fmaf(sc[kb][j][r], kLog2e, mneg));
         }
     }
-    return true;
-}
 
-// The same for PRE scores, which are relative to the reference already
-// (log2 units): the row max mt of S - m. Where it exceeds 8 the reference
-// moves up by mt, and O, the sum and the pending scores follow it (later
-// halves start their S accumulators from the new -m).
-static __device__ __forceinline__ bool update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
-                                               floatx4 (&o)[8][NQ], SBlk &s, floatx4 (&negm)[NQ]) {
-    bool over = false;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) over = over || lm[j] > 8.0f;
-    if (!__ballot(over)) return false;
-    {
-#pragma unroll
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+    // Add the fp16 probabilities (the very values the PV product weights) to the
+    // lane's running sums, two per dot instruction with fp32 accumulation.
+    static __device__ __forceinline__ void add_row_sums(const half8 (&pf)[NQ], float (&l_run)[NQ]) {
+        const half2v one = {(half_t)1.0f, (half_t)1.0f};
+    #pragma unroll
+        for (int j = 0; j < NQ; ++j)
+    #pragma unroll
+            for (int i = 0; i < 8; i += 2)
+                l_run[j] = __builtin_amdgcn_fdot2(half2v{pf[j][i], pf[j][i + 1]}, one, l_run[j], false);
+    }
+
+    // max(v) over lanes i, i ^ 16, i ^ 32, i ^ 48 (the four lanes that hold one
+    // query's keys). v_permlane16_swap trades the odd 16-lane rows of one
+    // register with the even rows of the other; applied to two copies of v it
+    // yields v of lane i and of lane i ^ 16 in every lane i.
+    static __device__ __forceinline__ float max_over_key_lanes(float v) {
+        v = wave_max_across_halves(v);
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+
+    // Each lane's maximum over its own 8 scores of every query block, for key
+    // half `half`, masking keys past skv. The row maximum is that over the four
+    // lanes of the query (max_over_key_lanes).
+    template <bool MASK>
+    static __device__ __forceinline__ void local_max(SBlk &s, int half, int skv, int g, float (&lm)[NQ]) {
+        if (MASK) {
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool out = 32 * half + 8 * g + 4 * kb + r >= skv;
+    #pragma unroll
+                    for (int j = 0; j < NQ; ++j)
+                        if (out) s[kb][j][r] = -INFINITY;
+                }
+        }
+    #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            const float mt = max_over_key_lanes(lm[j]);
-            const float delta = mt > 8.0f ? mt : 0.0f;
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            m_run[j] += delta;
-            l_run[j] *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb][j] -= delta;
-            negm[j] = splat4(-m_run[j]);
+            // three-operand max chains: four instructions for eight values
+            const float a = fmaxf(fmaxf(s[0][j][0], s[0][j][1]), s[0][j][2]);
+            const float b = fmaxf(fmaxf(s[0][j][3], s[1][j][0]), s[1][j][1]);
+            lm[j] = fmaxf(fmaxf(fmaxf(a, b), s[1][j][2]), s[1][j][3]);
         }
     }
-    return true;
-}
 
-struct State {
-    floatx4 o[8][NQ];  // O^T accumulators [head-dim block][query block]
-    half8 qf[NQ][4];   // Q as B operands [query block][head-dim step]
-    floatx4 negm[NQ];  // PRE: -m, the start value of each S accumulation chain
-    float m_run[NQ], l_run[NQ];
-};
-
-// Half U of step t: O += V P over key half 2t+U (pf, from the half-step
-// before), the scores of key half 2t+U+1 into sc, and their P into pf (after
-// the rescale check, redone if the reference moved). STEADY: every half this
-// step touches and stage t+3 are full;
-// fr holds the next RA operands on entry and exit, running on into the next
-// stage, and stage t+3's direct loads go out at fixed points. Otherwise every
-// condition is checked and reads stay within the half.
-template <bool PRE, bool CAT, bool STEADY, int U>
-static __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (&pf)[NQ], State &st,
-                                          half8 (&fr)[RA]) {
-    const half_t *cur = c.rl + (t & 3) * SLOT;
-    const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
-    const int hv = 2 * t + U;  // key half of this PV
-    const bool has_pv = STEADY || hv < c.NH;
-    const bool has_s = STEADY || hv + 1 < c.NH;
-#pragma unroll
-    for (int n = 0; n < HFRAG; ++n) {
-        if (!(n < 8 ? has_s : has_pv)) continue;  // wave-uniform
-        half8 a;
-        if (STEADY) {
-            a = fr[n % RA];
-            const int m = U * HFRAG + n + RA;
-            fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
-            // stage t+3's direct loads go out a quarter of the way into each
-            // half-step (K, then V^T) rather than in one burst at the step's start
-            if (U == 0 && n == 4) issue_k_full<CAT>(c, t + 3);
-            if (U == 1 && n == 4) issue_v_full<CAT>(c, t + 3);
-        } else {
-            a = rd(cur + (U * HFRAG + n) * FRAG);
-        }
-        if (n < 8) {
-            const int kk = n >> 1, kb = n & 1;
-#pragma unroll
-            for (int j = 0; j < NQ; ++j)
-                sc[kb][j] = mfma16(a, st.qf[j][kk], kk == 0 ? (PRE ? st.negm[j] : floatx4{}) : sc[kb][j]);
-        } else {
-            const int mb = n - 8;
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) st.o[mb][j] = mfma16(a, pf[j], st.o[mb][j]);
-        }
-    }
-    if (has_pv) add_row_sums(pf, st.l_run);
-    if (has_s) {
-        float lm[NQ];
-        const int g = c.lane >> 4;
-        if (STEADY || 32 * (hv + 2) <= c.skv)
-            local_max<false>(sc, hv + 1, c.skv, g, lm);
-        else
-            local_max<true>(sc, hv + 1, c.skv, g, lm);
-        // P of the next half against the current reference, before the check:
-        // redone only when the check moves the reference
-        exp_and_pack<PRE>(sc, pf, st.m_run);
-        // keep that work ahead of the branch (in the block with the MFMAs),
-        // where the compiler would otherwise sink it into the no-rescale path
-        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
-        const bool moved = PRE ? update_max_rel(lm, st.m_run, st.l_run, st.o, sc, st.negm)
-                               : update_max(lm, st.m_run, st.l_run, st.o);
-        if (moved) exp_and_pack<PRE>(sc, pf, st.m_run);
-    }
-}
-
-// Stage s holds K of key halves 2s+1, 2s+2 and V^T of halves 2s, 2s+1; the
-// prologue loads K of half 0 as stage -1 (slot 3) and stages 0..2, and
-// computes S of half 0 and its row max. Step t (0 <= t < T) adds V P of
-// halves 2t, 2t+1 into O and computes S of halves 2t+1, 2t+2; it issues stage
-// t+3 into the slot that stage t-1 used (all of whose reads finished before
-// the barrier that ended step t-1) and ends by waiting for stage t+2 and a
-// barrier, so step t+1 may read stage t+1's operands ahead of that barrier.
-//
-// PRE (set when q holds q_scaled * log2(e), as the block's projection writes
-// it): the scores come out of the S MFMAs already as (S - m) log2(e) -- the
-// log2(e) factor rides in Q and the first MFMA of each S chain starts from
-// the accumulator value -m (negm, four copies of the row's reference) instead
-// of 0 -- so the softmax needs no per-score FMA; m_run is then kept in log2
-// units.
-template <bool PRE, bool CAT>
-static __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-    const int g = lane >> 4;
-
-    const int nqb = (a.sq + BQ - 1) / BQ;
-    const int per_split = nqb * a.num_heads;
-    // a key split, or one of several K/V blocks (both give a packed partial per part)
-    const bool blocks = !CAT && a.n_kv_blocks > 0;
-    const int split = (a.n_split > 1 || blocks) ? work / per_split : 0;
-    const int head = (work - split * per_split) / nqb;
-    const int qb = (work - split * per_split) % nqb;
-    const int key_base = a.n_split > 1 ? split * a.split_len : 0;
-    const int skv = blocks ? a.kv_len[split] : a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
-    const half_t *kbase = blocks ? a.kv_k[split] + (int64_t)head * a.kv_k_head_stride[split]
-                                 : a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D;
-    const half_t *vbase = blocks ? a.kv_vt[split] + (int64_t)head * a.kv_v_head_stride[split]
-                                 : a.vt + (int64_t)head * a.v_head_stride + key_base;
-    const int64_t vrs = CAT ? a.kv_v_row_stride[0] : blocks ? a.kv_v_row_stride[split] : a.v_row_stride;
-    float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
-    float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
-    const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
-    const int64_t lse_hs = a.lse_head_stride ? a.lse_head_stride : (int64_t)a.sq;
-
-    const half_t *qh = a.q + (int64_t)head * a.q_head_stride;
-    const int q0 = qb * BQ + wave * 16 * NQ;  // first query row of the wave
-    State st;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        const int qc = min(q0 + 16 * j + (lane & 15), a.sq - 1);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st.qf[j][kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 32 + 8 * g));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) st.o[mb][j] = floatx4{};
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        st.m_run[j] = -INFINITY;
-        st.l_run[j] = 0.0f;
-    }
-
-    Ctx c;
-    c.kh = reinterpret_cast<const char *>(kbase);
-    c.vh = reinterpret_cast<const char *>(vbase);
-    c.ring = smem;
-    c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
-    c.lo = load_offsets(vrs, wave, lane, CAT);
-    c.wave = wave;
-    c.lane = lane;
-    c.skv = skv;
-    c.NH = (skv + 31) / 32;
-    c.T = (skv + BN - 1) / BN;
-    c.vrs = vrs;
-    c.a = &a;
-    c.head = head;
-    c.key_base = key_base;
-    c.lg_len = a.kv_lg_len;
-    const int T = c.T;
-
-    if (T > 0) {
-        SBlk sa;
-        half8 pf[NQ];
-        issue_stage<CAT>(c, -1);
-        issue_stage<CAT>(c, 0);
-        issue_stage<CAT>(c, 1);
-        wait_vm_lgkm(issue_stage<CAT>(c, 2));  // stages -1, 0, 1 complete
-        barrier_no_fence();
+    // Given the lanes' local maxima lm of the next scores: where some row's max
+    // grew by more than 2^8, raise its reference to the new row max and rescale O
+    // and the running sum to it. A lane whose own scores stay within 2^8 of the
+    // reference says nothing about the rest of its row, so the row maxima (a
+    // reduction over four lanes) are formed only when some lane of the wave is
+    // over; otherwise every score of the wave is within 2^8 and nothing changes.
+    static __device__ __forceinline__ bool update_max(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+                                               floatx4 (&o)[8][NQ]) {
+        bool over = false;
+    #pragma unroll
+        for (int j = 0; j < NQ; ++j) over = over || lm[j] > m_run[j] + kRescaleTau;
+        if (!__ballot(over)) return false;
         {
-            // S of key half 0 from stage -1's second K half (slot 3)
-            const half_t *k0 = c.rl + 3 * SLOT + HFRAG * FRAG;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const half8 f = rd(k0 + n * FRAG);
-                const int kk = n >> 1, kb = n & 1;
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) sa[kb][j] = mfma16(f, st.qf[j][kk], kk == 0 ? floatx4{} : sa[kb][j]);
-            }
-        }
-        float lm[NQ];
-        if (32 <= skv)
-            local_max<false>(sa, 0, skv, g, lm);
-        else
-            local_max<true>(sa, 0, skv, g, lm);
-        if (PRE) {
-            // the first half sets the reference: its scores came out relative to 0
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 const float mt = max_over_key_lanes(lm[j]);
-                st.m_run[j] = mt;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) sa[kb][j] -= mt;
-                st.negm[j] = splat4(-mt);
+                const float m_new = mt > m_run[j] + kRescaleTau ? mt : m_run[j];
+                const float alpha = __builtin_amdgcn_exp2f((m_run[j] - m_new) * kLog2e);
+                m_run[j] = m_new;
+                l_run[j] *= alpha;
+    #pragma unroll
+                for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
             }
-        } else {
-            update_max(lm, st.m_run, st.l_run, st.o);
         }
-        exp_and_pack<PRE>(sa, pf, st.m_run);
-        // Step 0 refills slot 3: every wave must be done reading it.
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
-        barrier_no_fence();
+        return true;
+    }
 
-        // Step t is steady when stage t+3 is full: 64t + 288 <= skv.
-        const int n_steady = skv >= 288 ? (skv - 288) / BN + 1 : 0;
-        half8 fr[RA];
-        int t = 0;
-        if (n_steady > 0) {
-#pragma unroll
-            for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
-            for (; t < n_steady; ++t) {
-                half_step<PRE, CAT, true, 0>(c, t, sa, pf, st, fr);
-                half_step<PRE, CAT, true, 1>(c, t, sa, pf, st, fr);
-                __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
-                barrier_no_fence();
+    // The same for PRE scores, which are relative to the reference already
+    // (log2 units): the row max mt of S - m. Where it exceeds 8 the reference
+    // moves up by mt, and O, the sum and the pending scores follow it (later
+    // halves start their S accumulators from the new -m).
+    static __device__ __forceinline__ bool update_max_rel(const float (&lm)[NQ], float (&m_run)[NQ], float (&l_run)[NQ],
+                                                   floatx4 (&o)[8][NQ], SBlk &s, floatx4 (&negm)[NQ]) {
+        bool over = false;
+    #pragma unroll
+        for (int j = 0; j < NQ; ++j) over = over || lm[j] > 8.0f;
+        if (!__ballot(over)) return false;
+        {
+    #pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const float mt = max_over_key_lanes(lm[j]);
+                const float delta = mt > 8.0f ? mt : 0.0f;
+                const float alpha = __builtin_amdgcn_exp2f(-delta);
+                m_run[j] += delta;
+                l_run[j] *= alpha;
+    #pragma unroll
+                for (int mb = 0; mb < 8; ++mb) o[mb][j] *= alpha;
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb) s[kb][j] -= delta;
+                negm[j] = splat4(-m_run[j]);
             }
         }
-        for (; t < T; ++t) {
-            const int inflight = issue_stage<CAT>(c, t + 3);
-            half_step<PRE, CAT, false, 0>(c, t, sa, pf, st, fr);
-            half_step<PRE, CAT, false, 1>(c, t, sa, pf, st, fr);
-            if (t + 1 < T) {
-                wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
-                barrier_no_fence();
+        return true;
+    }
+
+    struct State {
+        floatx4 o[8][NQ];  // O^T accumulators [head-dim block][query block]
+        half8 qf[NQ][4];   // Q as B operands [query block][head-dim step]
+        floatx4 negm[NQ];  // PRE: -m, the start value of each S accumulation chain
+        float m_run[NQ], l_run[NQ];
+    };
+
+    // Half U of step t: O += V P over key half 2t+U (pf, from the half-step
+    // before), the scores of key half 2t+U+1 into sc, and their P into pf (after
+    // the rescale check, redone if the reference moved). STEADY: every half this
+    // step touches and stage t+3 are full;
+    // fr holds the next RA operands on entry and exit, running on into the next
+    // stage, and stage t+3's direct loads go out at fixed points. Otherwise every
+    // condition is checked and reads stay within the half.
+    template <bool PRE, bool CAT, bool STEADY, int U>
+    static __device__ __forceinline__ void half_step(const Ctx &c, int t, SBlk &sc, half8 (&pf)[NQ], State &st,
+                                              half8 (&fr)[RA]) {
+        const half_t *cur = c.rl + (t & 3) * SLOT;
+        const half_t *nxt = c.rl + ((t + 1) & 3) * SLOT;
+        const int hv = 2 * t + U;  // key half of this PV
+        const bool has_pv = STEADY || hv < c.NH;
+        const bool has_s = STEADY || hv + 1 < c.NH;
+    #pragma unroll
+        for (int n = 0; n < HFRAG; ++n) {
+            if (!(n < 8 ? has_s : has_pv)) continue;  // wave-uniform
+            half8 a;
+            if (STEADY) {
+                a = fr[n % RA];
+                const int m = U * HFRAG + n + RA;
+                fr[n % RA] = rd(m < 2 * HFRAG ? cur + m * FRAG : nxt + (m - 2 * HFRAG) * FRAG);
+                // stage t+3's direct loads go out a quarter of the way into each
+                // half-step (K, then V^T) rather than in one burst at the step's start
+                if (U == 0 && n == 4) issue_k_full<CAT>(c, t + 3);
+                if (U == 1 && n == 4) issue_v_full<CAT>(c, t + 3);
+            } else {
+                a = rd(cur + (U * HFRAG + n) * FRAG);
             }
+            if (n < 8) {
+                const int kk = n >> 1, kb = n & 1;
+    #pragma unroll
+                for (int j = 0; j < NQ; ++j)
+                    sc[kb][j] = mfma16(a, st.qf[j][kk], kk == 0 ? (PRE ? st.negm[j] : floatx4{}) : sc[kb][j]);
+            } else {
+                const int mb = n - 8;
+    #pragma unroll
+                for (int j = 0; j < NQ; ++j) st.o[mb][j] = mfma16(a, pf[j], st.o[mb][j]);
+            }
+        }
+        if (has_pv) add_row_sums(pf, st.l_run);
+        if (has_s) {
+            float lm[NQ];
+            const int g = c.lane >> 4;
+            if (STEADY || 32 * (hv + 2) <= c.skv)
+                local_max<false>(sc, hv + 1, c.skv, g, lm);
+            else
+                local_max<true>(sc, hv + 1, c.skv, g, lm);
+            // P of the next half against the current reference, before the check:
+            // redone only when the check moves the reference
+            exp_and_pack<PRE>(sc, pf, st.m_run);
+            // keep that work ahead of the branch (in the block with the MFMAs),
+            // where the compiler would otherwise sink it into the no-rescale path
+            asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
+            const bool moved = PRE ? update_max_rel(lm, st.m_run, st.l_run, st.o, sc, st.negm)
+                                   : update_max(lm, st.m_run, st.l_run, st.o);
+            if (moved) exp_and_pack<PRE>(sc, pf, st.m_run);
         }
     }
 
-    // ---- epilogue: combine the four lane groups' sums, normalise, stage the
-    // wave's rows through LDS and store whole rows.
-    const bool empty = skv == 0;
-    float inv[NQ], l_tot[NQ];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        float l = st.l_run[j];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        l_tot[j] = l;
-        inv[j] = empty ? 0.0f : 1.0f / l;
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-    barrier_no_fence();  // every wave is done with the ring
-    const int qr = lane & 15;
-    if (o32) {
-        float *stg = reinterpret_cast<float *>(smem) + wave * 16 * OP32;
-#pragma unroll
+    // Stage s holds K of key halves 2s+1, 2s+2 and V^T of halves 2s, 2s+1; the
+    // prologue loads K of half 0 as stage -1 (slot 3) and stages 0..2, and
+    // computes S of half 0 and its row max. Step t (0 <= t < T) adds V P of
+    // halves 2t, 2t+1 into O and computes S of halves 2t+1, 2t+2; it issues stage
+    // t+3 into the slot that stage t-1 used (all of whose reads finished before
+    // the barrier that ended step t-1) and ends by waiting for stage t+2 and a
+    // barrier, so step t+1 may read stage t+1's operands ahead of that barrier.
+    //
+    // PRE (set when q holds q_scaled * log2(e), as the block's projection writes
+    // it): the scores come out of the S MFMAs already as (S - m) log2(e) -- the
+    // log2(e) factor rides in Q and the first MFMA of each S chain starts from
+    // the accumulator value -m (negm, four copies of the row's reference) instead
+    // of 0 -- so the softmax needs no per-score FMA; m_run is then kept in log2
+    // units.
+    template <bool PRE, bool CAT>
+    static __device__ __forceinline__ void attend_item(const FlashArgs &a, int work, char *smem) {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+        const int g = lane >> 4;
+
+        const int nqb = (a.sq + BQ - 1) / BQ;
+        const int per_split = nqb * a.num_heads;
+        // a key split, or one of several K/V blocks (both give a packed partial per part)
+        const bool blocks = !CAT && a.n_kv_blocks > 0;
+        const int split = (a.n_split > 1 || blocks) ? work / per_split : 0;
+        const int head = (work - split * per_split) / nqb;
+        const int qb = (work - split * per_split) % nqb;
+        const int key_base = a.n_split > 1 ? split * a.split_len : 0;
+        const int skv = blocks ? a.kv_len[split] : a.n_split > 1 ? min(a.split_len, a.skv - key_base) : a.skv;
+        const half_t *kbase = blocks ? a.kv_k[split] + (int64_t)head * a.kv_k_head_stride[split]
+                                     : a.k + (int64_t)head * a.k_head_stride + (int64_t)key_base * D;
+        const half_t *vbase = blocks ? a.kv_vt[split] + (int64_t)head * a.kv_v_head_stride[split]
+                                     : a.vt + (int64_t)head * a.v_head_stride + key_base;
+        const int64_t vrs = CAT ? a.kv_v_row_stride[0] : blocks ? a.kv_v_row_stride[split] : a.v_row_stride;
+        float *o32 = a.o32 ? a.o32 + (int64_t)split * a.num_heads * a.sq * D : nullptr;
+        float *lse_out = a.lse ? a.lse + (int64_t)split * a.num_heads * a.sq : nullptr;
+        const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
+        const int64_t lse_hs = a.lse_head_stride ? a.lse_head_stride : (int64_t)a.sq;
+
+        const half_t *qh = a.q + (int64_t)head * a.q_head_stride;
+        const int q0 = qb * BQ + wave * 16 * NQ;  // first query row of the wave
+        State st;
+    #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            const int qj = q0 + 16 * j;
-            const int rows = min(16, a.sq - qj);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-                *reinterpret_cast<floatx4 *>(stg + qr * OP32 + 16 * mb + 4 * g) = st.o[mb][j] * inv[j];
-            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-            __builtin_amdgcn_wave_barrier();
-            float *dst = o32 + (int64_t)head * o32_hs + (int64_t)qj * D;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 2 * i + (lane >> 5), chunk = lane & 31;
-                if (row < rows)
-                    *reinterpret_cast<floatx4 *>(dst + (int64_t)row * D + 4 * chunk) =
-                        *reinterpret_cast<const floatx4 *>(stg + row * OP32 + 4 * chunk);
-            }
-            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-            __builtin_amdgcn_wave_barrier();
+            const int qc = min(q0 + 16 * j + (lane & 15), a.sq - 1);
+    #pragma unroll
+            for (int kk = 0; kk < 4; ++kk) st.qf[j][kk] = as_half8(ldg16(qh + (int64_t)qc * D + kk * 32 + 8 * g));
         }
-    }
-    if (a.o16) {
-        half_t *stg = reinterpret_cast<half_t *>(smem) + wave * 16 * NQ * OP16;
-#pragma unroll
-        for (int j = 0; j < NQ; ++j)
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                half4 v;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = (half_t)(st.o[mb][j][r] * inv[j]);
-                *reinterpret_cast<half4 *>(stg + (16 * j + qr) * OP16 + 16 * mb + 4 * g) = v;
+    #pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+    #pragma unroll
+            for (int j = 0; j < NQ; ++j) st.o[mb][j] = floatx4{};
+    #pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            st.m_run[j] = -INFINITY;
+            st.l_run[j] = 0.0f;
+        }
+
+        Ctx c;
+        c.kh = reinterpret_cast<const char *>(kbase);
+        c.vh = reinterpret_cast<const char *>(vbase);
+        c.ring = smem;
+        c.rl = reinterpret_cast<const half_t *>(smem) + 8 * lane;
+        c.lo = load_offsets(vrs, wave, lane, CAT);
+        c.wave = wave;
+        c.lane = lane;
+        c.skv = skv;
+        c.NH = (skv + 31) / 32;
+        c.T = (skv + BN - 1) / BN;
+        c.vrs = vrs;
+        c.a = &a;
+        c.head = head;
+        c.key_base = key_base;
+        c.lg_len = a.kv_lg_len;
+        const int T = c.T;
+
+        if (T > 0) {
+            SBlk sa;
+            half8 pf[NQ];
+            issue_stage<CAT>(c, -1);
+            issue_stage<CAT>(c, 0);
+            issue_stage<CAT>(c, 1);
+            wait_vm_lgkm(issue_stage<CAT>(c, 2));  // stages -1, 0, 1 complete
+            barrier_no_fence();
+            {
+                // S of key half 0 from stage -1's second K half (slot 3)
+                const half_t *k0 = c.rl + 3 * SLOT + HFRAG * FRAG;
+    #pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const half8 f = rd(k0 + n * FRAG);
+                    const int kk = n >> 1, kb = n & 1;
+    #pragma unroll
+                    for (int j = 0; j < NQ; ++j) sa[kb][j] = mfma16(f, st.qf[j][kk], kk == 0 ? floatx4{} : sa[kb][j]);
+                }
             }
+            float lm[NQ];
+            if (32 <= skv)
+                local_max<false>(sa, 0, skv, g, lm);
+            else
+                local_max<true>(sa, 0, skv, g, lm);
+            if (PRE) {
+                // the first half sets the reference: its scores came out relative to 0
+    #pragma unroll
+                for (int j = 0; j < NQ; ++j) {
+                    const float mt = max_over_key_lanes(lm[j]);
+                    st.m_run[j] = mt;
+    #pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) sa[kb][j] -= mt;
+                    st.negm[j] = splat4(-mt);
+                }
+            } else {
+                update_max(lm, st.m_run, st.l_run, st.o);
+            }
+            exp_and_pack<PRE>(sa, pf, st.m_run);
+            // Step 0 refills slot 3: every wave must be done reading it.
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+            barrier_no_fence();
+
+            // Step t is steady when stage t+3 is full: 64t + 288 <= skv.
+            const int n_steady = skv >= 288 ? (skv - 288) / BN + 1 : 0;
+            half8 fr[RA];
+            int t = 0;
+            if (n_steady > 0) {
+    #pragma unroll
+                for (int n = 0; n < RA; ++n) fr[n] = rd(c.rl + n * FRAG);
+                for (; t < n_steady; ++t) {
+                    half_step<PRE, CAT, true, 0>(c, t, sa, pf, st, fr);
+                    half_step<PRE, CAT, true, 1>(c, t, sa, pf, st, fr);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_only(4));  // stage t+2 has landed
+                    barrier_no_fence();
+                }
+            }
+            for (; t < T; ++t) {
+                const int inflight = issue_stage<CAT>(c, t + 3);
+                half_step<PRE, CAT, false, 0>(c, t, sa, pf, st, fr);
+                half_step<PRE, CAT, false, 1>(c, t, sa, pf, st, fr);
+                if (t + 1 < T) {
+                    wait_vm_lgkm(inflight);  // stage t+2 complete (and its register-path stores)
+                    barrier_no_fence();
+                }
+            }
+        }
+
+        // ---- epilogue: combine the four lane groups' sums, normalise, stage the
+        // wave's rows through LDS and store whole rows.
+        const bool empty = skv == 0;
+        float inv[NQ], l_tot[NQ];
+    #pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float l = st.l_run[j];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            l_tot[j] = l;
+            inv[j] = empty ? 0.0f : 1.0f / l;
+        }
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-        __builtin_amdgcn_wave_barrier();
-        const int rows = min(16 * NQ, a.sq - q0);
-        half_t *dst = a.o16 + (int64_t)q0 * a.o16_ld + (int64_t)head * D;
-#pragma unroll
-        for (int i = 0; i < 4 * NQ; ++i) {
-            const int row = 4 * i + (lane >> 4), chunk = lane & 15;
-            if (row < rows)
-                *reinterpret_cast<u32x4 *>(dst + (int64_t)row * a.o16_ld + 8 * chunk) =
-                    *reinterpret_cast<const u32x4 *>(stg + row * OP16 + 8 * chunk);
+        barrier_no_fence();  // every wave is done with the ring
+        const int qr = lane & 15;
+        if (o32) {
+            float *stg = reinterpret_cast<float *>(smem) + wave * 16 * OP32;
+    #pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int qj = q0 + 16 * j;
+                const int rows = min(16, a.sq - qj);
+    #pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+                    *reinterpret_cast<floatx4 *>(stg + qr * OP32 + 16 * mb + 4 * g) = st.o[mb][j] * inv[j];
+                __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+                __builtin_amdgcn_wave_barrier();
+                float *dst = o32 + (int64_t)head * o32_hs + (int64_t)qj * D;
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = 2 * i + (lane >> 5), chunk = lane & 31;
+                    if (row < rows)
+                        *reinterpret_cast<floatx4 *>(dst + (int64_t)row * D + 4 * chunk) =
+                            *reinterpret_cast<const floatx4 *>(stg + row * OP32 + 4 * chunk);
+                }
+                __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+                __builtin_amdgcn_wave_barrier();
+            }
         }
-    }
-    if (lse_out && g == 0) {
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const int q = q0 + 16 * j + qr;
-            if (q < a.sq) {
-                // natural-log LSE; __builtin_amdgcn_logf is log2
-                const float lse = PRE ? (st.m_run[j] + __builtin_amdgcn_logf(l_tot[j])) * kLn2
-                                      : st.m_run[j] + __builtin_amdgcn_logf(l_tot[j]) * kLn2;
-                lse_out[(int64_t)head * lse_hs + q] = empty ? -INFINITY : lse;
+        if (a.o16) {
+            half_t *stg = reinterpret_cast<half_t *>(smem) + wave * 16 * NQ * OP16;
+    #pragma unroll
+            for (int j = 0; j < NQ; ++j)
+    #pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    half4 v;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = (half_t)(st.o[mb][j][r] * inv[j]);
+                    *reinterpret_cast<half4 *>(stg + (16 * j + qr) * OP16 + 16 * mb + 4 * g) = v;
+                }
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+            __builtin_amdgcn_wave_barrier();
+            const int rows = min(16 * NQ, a.sq - q0);
+            half_t *dst = a.o16 + (int64_t)q0 * a.o16_ld + (int64_t)head * D;
+    #pragma unroll
+            for (int i = 0; i < 4 * NQ; ++i) {
+                const int row = 4 * i + (lane >> 4), chunk = lane & 15;
+                if (row < rows)
+                    *reinterpret_cast<u32x4 *>(dst + (int64_t)row * a.o16_ld + 8 * chunk) =
+                        *reinterpret_cast<const u32x4 *>(stg + row * OP16 + 8 * chunk);
+            }
+        }
+        if (lse_out && g == 0) {
+    #pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int q = q0 + 16 * j + qr;
+                if (q < a.sq) {
+                    // natural-log LSE; __builtin_amdgcn_logf is log2
+                    const float lse = PRE ? (st.m_run[j] + __builtin_amdgcn_logf(l_tot[j])) * kLn2
+                                          : st.m_run[j] + __builtin_amdgcn_logf(l_tot[j]) * kLn2;
+                    lse_out[(int64_t)head * lse_hs + q] = empty ? -INFINITY : lse;
+                }
             }
         }
     }
-}
 
 };  // struct Rows
 
