@@ -14,7 +14,8 @@
 // Design (MI355X):
 // * One workgroup = 384 query rows of one head, 8 waves (2 per SIMD), 48 rows
 //   per wave as three 16-row blocks; K and V^T stages of 64 keys, worked in
-//   two 32-key halves.
+//   two 32-key halves. A 256-row form (two 16-row blocks per wave) serves
+//   grids that fill the CUs better in smaller pieces.
 // * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16, Q held in
 //   registers as the B operand of S. Every K or V^T fragment read from LDS
 //   feeds three MFMAs (one per query block), so a wave moves two thirds of
@@ -42,6 +43,9 @@
 //   16-byte chunks of whole lines.
 // * Blocks are remapped so each XCD works through a contiguous range of
 //   (head, query block) items and its concurrent workgroups share K/V in L2.
+// * Every fp16 attention call is planned (plan_attention_f16): the workgroup
+//   size, and a key-split tail for the last query rows of each head when the
+//   last round of workgroups would leave CUs idle, merged by LSE.
 
 #include <algorithm>
 #include <atomic>
