@@ -279,6 +279,12 @@ __device__ __forceinline__ void wait_vm_lgkm(int n) {
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
 }
 
+// The larger of two scores as IEEE maximum (a NaN wins): gfx950 forms
+// v_maximum3_f32 from chains of it directly, where fmaxf's maxNum would first
+// quiet every MFMA result with an extra v_max_f32 per operand. The two agree on
+// every non-NaN input, and a NaN score makes its row's output NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ half8 rd(const half_t *p) { return *reinterpret_cast<const half8 *>(p); }
 
 // Everything that depends on the number NQ of 16-row query blocks per wave:
@@ -328,7 +334,7 @@ struct Rows {
     static __device__ __forceinline__ float max_over_key_lanes(float v) {
         v = wave_max_across_halves(v);
         const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
     }
 
     // Each lane's maximum over its own 8 scores of every query block, for key
@@ -350,9 +356,9 @@ struct Rows {
     #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             // three-operand max chains: four instructions for eight values
-            const float a = fmaxf(fmaxf(s[0][j][0], s[0][j][1]), s[0][j][2]);
-            const float b = fmaxf(fmaxf(s[0][j][3], s[1][j][0]), s[1][j][1]);
-            lm[j] = fmaxf(fmaxf(fmaxf(a, b), s[1][j][2]), s[1][j][3]);
+            const float a = vmax(vmax(s[0][j][0], s[0][j][1]), s[0][j][2]);
+            const float b = vmax(vmax(s[0][j][3], s[1][j][0]), s[1][j][1]);
+            lm[j] = vmax(vmax(vmax(a, b), s[1][j][2]), s[1][j][3]);
         }
     }
 

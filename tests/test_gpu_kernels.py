@@ -63,6 +63,33 @@ def test_planned_split_tail_vs_oracle():
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "planned launch not deterministic"
 
 
+@pytest.mark.parametrize("ramp", [False, True])
+def test_partial_f16_384_row_workgroups_vs_oracle(ramp):
+    # 40 heads of 2000 query rows: 240 workgroups of 384 rows fit one round of
+    # 256 CUs and 320 of 256 rows would not, so the launch plan takes the
+    # 384-row form (the small shapes above get 256-row workgroups). Ragged in
+    # both query rows (2000 = 5 x 384 + 80) and keys, with peaked scores, or
+    # with keys ordered so that every tile moves the running max by far more
+    # than the 2^8 lazy-rescale threshold.
+    h, sq, d = 40, 2000, 128
+    skv = 640 if ramp else 1000
+    say(f"partial f16 384-row workgroups H={h} sq={sq} skv={skv} ramp={ramp}")
+    if ramp:
+        rng = np.random.default_rng(15)
+        q = np.full((h, sq, d), 0.05, np.float16)
+        base = rng.standard_normal((h, skv, d)).astype(np.float32) * 0.1
+        k = (base + np.linspace(0.0, 30.0, skv, dtype=np.float32)[None, :, None]).astype(np.float16)
+        v = rng.standard_normal((h, skv, d)).astype(np.float16)
+    else:
+        q, k, v = attention_inputs(h, sq, skv, d, seed=14, score_std=8.0)
+    vt = to_vt(v)
+    o, lse = partial(dev(q), dev(k), dev(vt), sq, skv, vt.shape[2])
+    heads = [0, 17, h - 1]
+    o_ref, lse_ref = oracle.partial_attention(q[heads], k[heads], v[heads])
+    assert_close(host(o)[heads], o_ref, what="o_part (384-row workgroups)")
+    assert_close(host(lse)[heads], lse_ref, what="lse_part (384-row workgroups)")
+
+
 def test_partial_f16_peaked_scores_exercise_rescale():
     # score std 8: running maxima keep growing by more than the 2^8 lazy-rescale threshold
     say("partial f16 peaked scores")

@@ -172,11 +172,12 @@ def test_ring_equal_device_blocks_read_as_one_sequence():
     assert rel_l2(host(lse), host(lse2)) <= REL_L2_SPLIT
 
 
-@pytest.mark.parametrize("hh,sq,blen,nb", [(3, 77, 64, 5), (1, 400, 512, 16), (2, 1, 128, 3)])
+@pytest.mark.parametrize("hh,sq,blen,nb", [(3, 77, 64, 5), (1, 400, 512, 16), (2, 1, 128, 3), (40, 2000, 256, 4)])
 def test_ring_equal_device_blocks_edge_shapes(hh, sq, blen, nb):
     # the one-sequence path at its edges: the shortest block (64 keys), the most
-    # blocks one launch takes (16), a single query row; all rows against the oracle
-    # and bit for bit against one partial over the concatenated keys
+    # blocks one launch takes (16), a single query row, and 40 heads of 2000 rows
+    # (384-row workgroups; the others take 256-row ones); all rows against the
+    # oracle and bit for bit against one partial over the concatenated keys
     d = 128
     lens = [blen] * nb
     say(f"ring, equal device blocks: H={hh} sq={sq} {nb} x {blen}")
