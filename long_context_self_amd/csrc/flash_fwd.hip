@@ -785,46 +785,58 @@ int cu_count() {
 // length, run in rounds of one workgroup per CU; a last round that is only
 // partly full leaves CUs idle for a whole workgroup time (10% of the time at
 // 32 heads and seq 16384). The plan keeps the first query blocks of every
-// head whole and splits the last tb blocks of every head into k key ranges,
-// so the tail runs as short workgroups that fill their rounds; their
-// partials are merged by LSE. It takes the (tb, k) of least modelled time,
-// counting the merge traffic and the extra launches, and no split unless
-// that gains at least 1% over the plain launch.
+// head whole and runs the rows after them as a tail: in the other workgroup
+// size over all keys, or split into k key ranges whose partials are merged
+// by LSE, so that the tail's workgroups fill their rounds. It takes the plan
+// of least modelled time, counting the merge traffic and the extra launches,
+// and none unless it gains at least 1% over the plain launch.
 AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems) {
-    AttnPlan p{sq, 1, 0, 0, 0, kMaxNQ};
+    AttnPlan p{sq, 1, 0, 0, 0, kMaxNQ, kMaxNQ};
     if (num_heads <= 0 || sq <= 0 || skv <= 0) return p;
     const int64_t C = cu_count();
     auto rounds = [C](int64_t n) { return (double)((n + C - 1) / C); };
+    auto blocks = [](int rows, int nq) { return (rows + NWAVES * 16 * nq - 1) / (NWAVES * 16 * nq); };
+    auto item = [](int nq, int keys) {
+        return kItemPerKey * (nq == kMaxNQ ? 1.0 : kRows256Cost) * keys + kItemFixed;
+    };
     // the plain launch of 384-row workgroups is what any other plan must beat by 1%
-    double best = 0.99 * rounds((int64_t)((sq + 383) / 384) * num_heads) * (kItemPerKey * skv + kItemFixed);
+    double best = 0.99 * rounds((int64_t)blocks(sq, kMaxNQ) * num_heads) * item(kMaxNQ, skv);
     for (int nq = kMaxNQ; nq >= 2; --nq) {
         const int bq = NWAVES * 16 * nq;
-        const double per_key = kItemPerKey * (nq == kMaxNQ ? 1.0 : kRows256Cost);
-        const int nqb = (sq + bq - 1) / bq;
-        const double t_item = per_key * skv + kItemFixed;
-        if (nq != kMaxNQ && rounds((int64_t)nqb * num_heads) * t_item < best) {
-            best = rounds((int64_t)nqb * num_heads) * t_item;
-            p = AttnPlan{sq, 1, 0, 0, 0, nq};
+        const int nqb = blocks(sq, nq);
+        if (nq != kMaxNQ && rounds((int64_t)nqb * num_heads) * item(nq, skv) < best) {
+            best = rounds((int64_t)nqb * num_heads) * item(nq, skv);
+            p = AttnPlan{sq, 1, 0, 0, 0, nq, nq};
         }
-        if (skv < 2 * kMinSplitKeys) continue;
         const int tb_max = (int)std::min<int64_t>(nqb, 2 * C / num_heads + 1);
         for (int tb = 1; tb <= nqb; ++tb) {
             if (tb > tb_max && tb != nqb) continue;
             const int main_rows = (nqb - tb) * bq;
             const int tail_rows = sq - main_rows;
-            for (int k = 2; k <= kMaxSplit; ++k) {
-                const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
-                if (len < kMinSplitKeys) break;
-                const int ke = (skv + len - 1) / len;
-                const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
-                if (o_el > max_o_elems) break;
-                const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
-                const double t = rounds((int64_t)(nqb - tb) * num_heads) * t_item +
-                                 rounds((int64_t)tb * num_heads * ke) * (per_key * len + kItemFixed) + merge +
-                                 kExtraLaunch;
-                if (t < best) {
-                    best = t;
-                    p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows, nq};
+            const double t_main = rounds((int64_t)(nqb - tb) * num_heads) * item(nq, skv);
+            for (int tq = kMaxNQ; tq >= 2; --tq) {
+                const int ntb = blocks(tail_rows, tq);
+                if (tq != nq) {  // the tail over all keys straight into the outputs: one more launch
+                    const double t = t_main + rounds((int64_t)ntb * num_heads) * item(tq, skv) + 0.5 * kExtraLaunch;
+                    if (t < best) {
+                        best = t;
+                        p = AttnPlan{main_rows, 1, 0, 0, 0, nq, tq};
+                    }
+                }
+                if (skv < 2 * kMinSplitKeys) continue;
+                for (int k = 2; k <= kMaxSplit; ++k) {
+                    const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
+                    if (len < kMinSplitKeys) break;
+                    const int ke = (skv + len - 1) / len;
+                    const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
+                    if (o_el > max_o_elems) break;
+                    const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
+                    const double t =
+                        t_main + rounds((int64_t)ntb * num_heads * ke) * item(tq, len) + merge + kExtraLaunch;
+                    if (t < best) {
+                        best = t;
+                        p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows, nq, tq};
+                    }
                 }
             }
         }
@@ -836,8 +848,8 @@ hipError_t launch_attention_f16(const FlashArgs &args, const AttnPlan &p, float 
                                 hipStream_t stream) {
     FlashArgs a = args;
     a.nq = p.nq;
-    if (p.n_split <= 1 || p.main_rows >= a.sq || a.n_split > 1 || (a.n_kv_blocks > 0 && !a.kv_concat) ||
-        (a.o16 && a.o32) || (!a.o16 && !a.o32) || !ws_o || !ws_lse)
+    if (p.main_rows >= a.sq || a.n_split > 1 || (a.n_kv_blocks > 0 && !a.kv_concat) || (a.o16 && a.o32) ||
+        (!a.o16 && !a.o32) || (p.n_split > 1 && (!ws_o || !ws_lse)))
         return launch_flash_fwd_f16(a, stream);
     hipError_t e = hipSuccess;
     const int64_t o32_hs = a.o32_head_stride ? a.o32_head_stride : (int64_t)a.sq * D;
@@ -852,8 +864,21 @@ hipError_t launch_attention_f16(const FlashArgs &args, const AttnPlan &p, float 
     }
     const int tail = a.sq - p.main_rows;
     FlashArgs t = a;
+    t.nq = p.tail_nq;
     t.q = a.q + (int64_t)p.main_rows * D;
     t.sq = tail;
+    if (p.n_split <= 1) {  // the tail rows over all keys, into the outputs
+        if (a.o16) t.o16 = a.o16 + (int64_t)p.main_rows * a.o16_ld;
+        if (a.o32) {
+            t.o32 = a.o32 + (int64_t)p.main_rows * D;
+            t.o32_head_stride = o32_hs;
+        }
+        if (a.lse) {
+            t.lse = a.lse + p.main_rows;
+            t.lse_head_stride = lse_hs;
+        }
+        return launch_flash_fwd_f16(t, stream);
+    }
     t.o16 = nullptr;
     t.o32 = ws_o;
     t.lse = ws_lse;

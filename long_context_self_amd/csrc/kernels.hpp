@@ -155,7 +155,8 @@ struct MergeArgs {
 struct AttnPlan {
     int main_rows, n_split, split_len;
     int64_t o_elems, lse_elems;
-    int nq;
+    int nq;       // 16-row query blocks per wave of the whole-key launch (3: 384-row workgroups, 2: 256)
+    int tail_nq;  // the same for the rows from main_rows on
 };
 
 // Workspace budgets of a key-split attention tail (floats of partial rows):

@@ -48,7 +48,7 @@ def test_planned_split_tail_vs_oracle():
     # 32 heads, 3500 query rows: 320 workgroups of 384 rows would leave the
     # second round of 256 CUs mostly idle, so the launch plan runs rows
     # [0, 3072) whole and splits the last 428 rows of every head over key
-    # ranges, merged by LSE. Both parts, and the border between them, against
+    # ranges (in 256-row workgroups), merged by LSE. Both parts, and the border between them, against
     # the oracle on two heads (all rows).
     h, sq, skv, d = 32, 3500, 3500, 128
     say(f"planned launch with a split tail: H={h} sq={sq} skv={skv}")
@@ -227,6 +227,29 @@ def test_row_chunk_is_bit_exact(a, b):
     o_c, lse_c = partial(qc, kd, vtd, b - a, skv, vt.shape[2])
     assert torch.equal(o_c, o_full[:, a:b])
     assert torch.equal(lse_c, lse_full[:, a:b])
+
+
+def test_whole_key_tail_in_256_row_workgroups_vs_oracle():
+    # 40 heads of 3100 rows over 1000 keys (too few to split): the launch plan
+    # runs rows [0, 2304) in 384-row workgroups (240, one round of 256 CUs) and
+    # the 796 rows after them over all keys in 256-row workgroups (160, one
+    # more round) straight into the outputs. Against the oracle on three heads,
+    # and row for row against runs of parts of the rows alone: [0, 1000) alone
+    # takes 256-row workgroups, yet its bits equal those the 384-row workgroups
+    # gave the same rows (no row's arithmetic depends on the rows beside it).
+    h, sq, skv, d = 40, 3100, 1000, 128
+    say(f"main launch + whole-key tail of the other workgroup size: H={h} sq={sq} skv={skv}")
+    q, k, v = attention_inputs(h, sq, skv, d, seed=16)
+    kd, vt = dev(k), to_vt(v)
+    vtd = dev(vt)
+    o, lse = partial(dev(q), kd, vtd, sq, skv, vt.shape[2])
+    heads = [0, 21, h - 1]
+    o_ref, lse_ref = oracle.partial_attention(q[heads], k[heads], v[heads])
+    assert_close(host(o)[heads], o_ref, what="o_part (main rows and whole-key tail)")
+    assert_close(host(lse)[heads], lse_ref, what="lse_part (main rows and whole-key tail)")
+    for a, b in [(0, 1000), (2304, 3100), (2200, 2400)]:
+        o_c, lse_c = partial(dev(np.ascontiguousarray(q[:, a:b])), kd, vtd, b - a, skv, vt.shape[2])
+        assert torch.equal(o_c, o[:, a:b]) and torch.equal(lse_c, lse[:, a:b]), f"rows [{a},{b}) alone differ"
 
 
 def test_two_runs_are_bit_identical():
