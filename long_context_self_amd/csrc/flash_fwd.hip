@@ -478,7 +478,10 @@ struct Rows {
             exp_and_pack<PRE>(sc, pf, st.m_run);
             // keep that work ahead of the branch (in the block with the MFMAs),
             // where the compiler would otherwise sink it into the no-rescale path
-            asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
+            if constexpr (NQ == 3)
+                asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
+            else
+                asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
             const bool moved = PRE ? update_max_rel(lm, st.m_run, st.l_run, st.o, sc, st.negm)
                                    : update_max(lm, st.m_run, st.l_run, st.o);
             if (moved) exp_and_pack<PRE>(sc, pf, st.m_run);
