@@ -43,9 +43,10 @@
 //   16-byte chunks of whole lines.
 // * Blocks are remapped so each XCD works through a contiguous range of
 //   (head, query block) items and its concurrent workgroups share K/V in L2.
-// * Every fp16 attention call is planned (plan_attention_f16): the workgroup
-//   size, and a key-split tail for the last query rows of each head when the
-//   last round of workgroups would leave CUs idle, merged by LSE.
+// * Every fp16 attention call is planned (plan_attention_f16): when the last
+//   round of workgroups would leave CUs idle, the last query rows of each head
+//   run as a tail, in the other workgroup size over all keys or split over key
+//   ranges and merged by LSE.
 
 #include <algorithm>
 #include <atomic>
@@ -709,7 +710,7 @@ struct Rows {
 
 };  // struct Rows
 
-// One workgroup per (key split, head, 128 NQ-row query block) item, remapped
+// One workgroup per (key split, head, query block of 128 NQ rows) item, remapped
 // so each XCD works through a contiguous range of items and its concurrent
 // workgroups share one head's K/V in L2.
 template <int NQ, bool PRE, bool CAT>
@@ -755,8 +756,8 @@ constexpr int kMinSplitKeys = 512;    // shortest key range worth a workgroup
 // Cost model of a plan, in seconds: a workgroup over L keys takes about
 // kItemPerKey * L (384 rows at the kernel's rate on one CU) plus a fixed
 // start-up and epilogue kItemFixed; the partials of a split tail are written
-// once and read once by the merge at about kMergeBw; the two extra launches
-// cost kExtraLaunch.
+// once and read once by the merge at about kMergeBw; the tail and merge
+// launches cost kExtraLaunch (a tail over all keys, with no merge, half that).
 constexpr double kItemPerKey = 3.95e-8, kItemFixed = 8e-6, kMergeBw = 4.0e12, kExtraLaunch = 1.5e-5;
 // A 256-row workgroup's time per key relative to a 384-row one (it moves more
 // LDS bytes per product: measured 0.71 at seq 65536, 0.75 at 8192).

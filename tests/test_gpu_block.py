@@ -101,10 +101,12 @@ def test_tiny_config_fp32_rank_share_four_chunks():
     blk.close()
 
 
-# The last case (40 heads of 2000 rows) runs its attention in 384-row
-# workgroups, which fit one round of 256 CUs; the others take 256-row ones.
+# 40 heads of 2000 rows run their attention in 384-row workgroups, which fit
+# one round of 256 CUs; 48 heads of 2000 rows run rows [0, 1920) so and the
+# last 80 rows of every head in 256-row workgroups over 4 key ranges, merged by
+# LSE; the others take 256-row workgroups.
 @pytest.mark.parametrize("seq,h,nh", [(1000, 512, 4), (300, 384, 3), (1, 256, 2), (7, 128, 1), (520, 1024, 8),
-                                      (2000, 256, 2), (2000, 5120, 40)])
+                                      (2000, 256, 2), (2000, 5120, 40), (2000, 6144, 48)])
 def test_block_f16_small_all_rows(seq, h, nh):
     _check_all_rows(seq, h, nh, np.float16, 5e-3, 2e-2)
 

@@ -172,6 +172,36 @@ def test_ring_equal_device_blocks_read_as_one_sequence():
     assert rel_l2(host(lse), host(lse2)) <= REL_L2_SPLIT
 
 
+@pytest.mark.parametrize("hh,sq,blen,nb,heads", [(40, 3100, 256, 4, [0, 17, 39]), (40, 2400, 512, 4, [0, 23, 39])])
+def test_ring_equal_device_blocks_main_launch_and_tail(hh, sq, blen, nb, heads):
+    # The one-sequence launch under the two tail plans: 40 heads of 3100 rows over
+    # 1024 keys run rows [0, 2304) in 384-row workgroups and the rest over all keys
+    # in 256-row ones; 40 heads of 2400 rows over 2048 keys run the last 96 rows in
+    # 256-row workgroups over 4 key ranges, merged by LSE. Against the oracle on
+    # three heads, and bit for bit against one partial over the concatenated keys.
+    d = 128
+    lens = [blen] * nb
+    say(f"ring, equal device blocks with a planned tail: H={hh} sq={sq} {nb} x {blen}")
+    q, k, v = attention_inputs(hh, sq, sum(lens), d, seed=60 + nb)
+    kb, vb = _blocks(k, v, lens)
+    qd = dev(q)
+    o, lse = _ring(qd, sq, kb, vb, lens, hh, d)
+    o_ref, lse_ref = oracle.partial_attention(q[heads], k[heads], v[heads])
+    got = host(o).reshape(sq, hh, d).transpose(1, 0, 2)
+    assert_close(got[heads], o_ref, what="ring O")
+    assert_close(host(lse)[heads], lse_ref, what="ring LSE")
+    skv = sum(lens)
+    ld = B.vt_ld(skv)
+    vt = np.zeros((hh, d, ld), dtype=np.float16)
+    vt[:, :, :skv] = v.transpose(0, 2, 1)
+    o32 = torch.empty((hh, sq, d), dtype=torch.float32, device="cuda")
+    l32 = torch.empty((hh, sq), dtype=torch.float32, device="cuda")
+    B.attn_partial_forward_vt(hh, d, qd, sq, sq * d, dev(k), skv, skv * d, dev(vt), d * ld, ld, o32, l32)
+    torch.cuda.synchronize()
+    o_cat = o32.transpose(0, 1).reshape(sq, hh * d).to(torch.float16)
+    assert torch.equal(o, o_cat) and torch.equal(lse, l32), "ring differs from one partial over the concatenated keys"
+
+
 @pytest.mark.parametrize("hh,sq,blen,nb", [(3, 77, 64, 5), (1, 400, 512, 16), (2, 1, 128, 3), (40, 2000, 256, 4)])
 def test_ring_equal_device_blocks_edge_shapes(hh, sq, blen, nb):
     # the one-sequence path at its edges: the shortest block (64 keys), the most
