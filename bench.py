@@ -686,8 +686,9 @@ def main() -> int:
     kernel_tflops = {n: fl[n] / (kern[n]["mean"] * 1e-3) / 1e12 for n in ("qkv", "attn", "oproj")}
     dom = max(("qkv", "attn", "oproj"), key=lambda n: kern[n]["mean"])
     names = {"qkv": "gemm_f16_nt (QKV projection, fused layout epilogue)",
-             "attn": "attention step: flash_fwd_f16_d128 over the whole-key query blocks, then over the "
-                     "key-split tail rows, then lse_merge of that tail (one launch when the plan does not split)",
+             "attn": "attention step: flash_fwd_f16_d128 over the whole-key query blocks (384 rows each), then over "
+                     "the tail rows in 256-row workgroups, split over key ranges and merged by lse_merge, or over "
+                     "all keys (as the launch plan picks for the shape)",
              "oproj": "gemm_f16_nt (output projection)"}
     counters = f"hbm_counters_seq{seq}_h{h}.txt"
     roofline = {"bound": "mfma", "kernel": names[dom], "achieved": kernel_tflops[dom], "peak": PEAK_F16_TFLOPS,
