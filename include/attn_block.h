@@ -233,10 +233,11 @@ attn_status_t attn_block_forward(attn_block_t *blk, const void *x, void *y, int6
  * for reuse). That pass reads and writes H*skv*d elements more than
  * attn_partial_forward_vt, which takes V^T directly. Calls on different
  * streams may overlap. In fp16, a call whose grid would leave a last round
- * of workgroups partly idle runs the last query rows of each head split over
- * key ranges and merges them by LSE (the same plan for the same num_heads, sq
- * and skv, in every partial entry point and in attn_ring_forward); those
- * partials, at most 64 MiB, come from the same pool.
+ * of workgroups partly idle runs the last query rows of each head as a tail
+ * of smaller workgroups, over all keys or split over key ranges and merged by
+ * LSE (the same plan for the same num_heads, sq and skv, in every partial
+ * entry point and in attn_ring_forward); split partials, at most 64 MiB, come
+ * from the same pool.
  * Pointers 16-byte aligned; head strides multiples of 8 (ATTN_F16) or 4
  * (ATTN_F32), q_head_stride >= sq*d and kv_head_stride >= skv*d when
  * num_heads > 1. sq = 0 enqueues nothing. skv = 0 writes o_part = 0 and
@@ -308,9 +309,10 @@ attn_status_t attn_partial_forward_noalloc(int num_heads, int head_dim, attn_dty
  *   lse          NULL or fp32 [H][seq], natural-log.
  * head_dim 128 (ATTN_F16) or 64/128 (ATTN_F32); pointers 16-byte aligned.
  * seq = 0 enqueues nothing. In fp16, when the grid would leave a last round
- * of workgroups partly idle, the last query rows of each head run split over
- * key ranges and are merged by LSE; those partials (at most 256 MiB) come from
- * the library's stream-ordered pool, allocated and released on `stream`.
+ * of workgroups partly idle, the last query rows of each head run as a tail of
+ * smaller workgroups, over all keys or split over key ranges and merged by LSE;
+ * split partials (at most 256 MiB) come from the library's stream-ordered
+ * pool, allocated and released on `stream`.
  * Errors: ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_OOM (the split
  * partials), ATTN_E_HIP.
  */
