@@ -1,6 +1,6 @@
-// Device-side building blocks shared by the gfx950 kernels: vector types, the
-// MFMA wrapper and its lane layouts (checked on an MI355X), XCD-aware block
-// remapping and small fp16 helpers.
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// 16-byte loads and stores, XCD-aware block remapping, wait-count encodings,
+// the bare workgroup barrier and a cross-lane max.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,28 +12,14 @@ namespace attnblk {
 typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// v_mfma_f32_32x32x16_f16: C[32x32] += A[32x16] * B[16x32].
-// Lane l supplies A row (l % 32), k = 8*(l/32) + j, j < 8, and B column
-// (l % 32) with the same k. Accumulator element 4*g + r of lane l is
-// C[8*g + 4*(l/32) + r][l % 32]. Any relabelling of k is allowed as long as
-// A and B use the same one (the sum over k does not depend on its order).
-__device__ __forceinline__ floatx16 mfma32(const half8 &a, const half8 &b, const floatx16 &c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ half8 as_half8(const u32x4 &v) {
     return __builtin_bit_cast(half8, v);
-}
-__device__ __forceinline__ u32x4 as_u32x4(const half8 &v) {
-    return __builtin_bit_cast(u32x4, v);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
