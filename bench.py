@@ -461,6 +461,8 @@ def run_ring_share(torch, B, hip, warmup, steps, seq=32768, h=4096, nh=32, ranks
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_self_amd", "csrc")
+# the sources that decide the attention step's launches and kernels (its HBM counters go stale with them)
+ATTN_SOURCES = ("flash_fwd.hip", "common.hpp", "lse_merge.hip", "launch_plan.hpp")
 
 
 def hbm_traffic(kernel: str, sources: tuple[str, ...], counters: str):
@@ -693,8 +695,7 @@ def main() -> int:
     counters = f"hbm_counters_seq{seq}_h{h}.txt"
     roofline = {"bound": "mfma", "kernel": names[dom], "achieved": kernel_tflops[dom], "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": kernel_tflops[dom] / PEAK_F16_TFLOPS,
-                "traffic": hbm_traffic("attention", ("flash_fwd.hip", "common.hpp", "lse_merge.hip"), counters)
-                if dom == "attn" else None,
+                "traffic": hbm_traffic("attention", ATTN_SOURCES, counters) if dom == "attn" else None,
                 "flops_per_launch": fl[dom], "avg_launch_ms": kern[dom]["mean"],
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated, "
                                 f"profiles/{counters})",

@@ -43,12 +43,11 @@
 //   16-byte chunks of whole lines.
 // * Blocks are remapped so each XCD works through a contiguous range of
 //   (head, query block) items and its concurrent workgroups share K/V in L2.
-// * Every fp16 attention call is planned (plan_attention_f16): when the last
-//   round of workgroups would leave CUs idle, the last query rows of each head
-//   run as a tail, in the other workgroup size over all keys or split over key
-//   ranges and merged by LSE.
+// * Every fp16 attention call is planned (plan_attention_f16, launch_plan.hpp):
+//   when the last round of workgroups would leave CUs idle, the last query
+//   rows of each head run as a tail, in the other workgroup size over all keys
+//   or split over key ranges and merged by LSE.
 
-#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -63,6 +62,9 @@ constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int kMaxNQ = 3;             // 16-row query blocks per wave: 3 (384-row workgroups) or 2 (256)
 constexpr int BN = 64;                // keys per stage
+static_assert(plan::kRowsPerNq == NWAVES * 16 && plan::kMaxNQ == kMaxNQ && plan::kKeyStep == BN &&
+                  plan::kHeadDim == D,
+              "the launch plan's shape constants are the kernel's");
 constexpr int FRAG = 64 * 8;          // halves in one MFMA operand fragment
 constexpr int HFRAG = 16;             // fragments per half-stage: 8 of K, then 8 of V^T
 constexpr int SLOT = 2 * HFRAG * FRAG;    // halves per ring slot
@@ -751,18 +753,6 @@ hipError_t launch_flash_fwd_f16(const FlashArgs &a, hipStream_t stream) {
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kMaxSplit = 16;         // key ranges of a split tail
-constexpr int kMinSplitKeys = 512;    // shortest key range worth a workgroup
-// Cost model of a plan, in seconds: a workgroup over L keys takes about
-// kItemPerKey * L (384 rows at the kernel's rate on one CU) plus a fixed
-// start-up and epilogue kItemFixed; the partials of a split tail are written
-// once and read once by the merge at about kMergeBw; the tail and merge
-// launches cost kExtraLaunch (a tail over all keys, with no merge, half that).
-constexpr double kItemPerKey = 3.95e-8, kItemFixed = 8e-6, kMergeBw = 4.0e12, kExtraLaunch = 1.5e-5;
-// A 256-row workgroup's time per key relative to a 384-row one (it moves more
-// LDS bytes per product: measured 0.71 at seq 65536, 0.75 at 8192).
-constexpr double kRows256Cost = 0.75;
-
 std::atomic<int> g_cus[kMaxDevices];
 
 // Compute units of the current device (256 on an MI355X).
@@ -785,67 +775,9 @@ int cu_count() {
 
 }  // namespace
 
-// The grid of a plain launch is H * ceil(sq / 384) workgroups of equal
-// length, run in rounds of one workgroup per CU; a last round that is only
-// partly full leaves CUs idle for a whole workgroup time (10% of the time at
-// 32 heads and seq 16384). The plan keeps the first query blocks of every
-// head whole and runs the rows after them as a tail: in the other workgroup
-// size over all keys, or split into k key ranges whose partials are merged
-// by LSE, so that the tail's workgroups fill their rounds. It takes the plan
-// of least modelled time, counting the merge traffic and the extra launches,
-// and none unless it gains at least 1% over the plain launch.
+// The plan for this device (launch_plan.hpp).
 AttnPlan plan_attention_f16(int num_heads, int sq, int skv, int64_t max_o_elems) {
-    AttnPlan p{sq, 1, 0, 0, 0, kMaxNQ, kMaxNQ};
-    if (num_heads <= 0 || sq <= 0 || skv <= 0) return p;
-    const int64_t C = cu_count();
-    auto rounds = [C](int64_t n) { return (double)((n + C - 1) / C); };
-    auto blocks = [](int rows, int nq) { return (rows + NWAVES * 16 * nq - 1) / (NWAVES * 16 * nq); };
-    auto item = [](int nq, int keys) {
-        return kItemPerKey * (nq == kMaxNQ ? 1.0 : kRows256Cost) * keys + kItemFixed;
-    };
-    // the plain launch of 384-row workgroups is what any other plan must beat by 1%
-    double best = 0.99 * rounds((int64_t)blocks(sq, kMaxNQ) * num_heads) * item(kMaxNQ, skv);
-    for (int nq = kMaxNQ; nq >= 2; --nq) {
-        const int bq = NWAVES * 16 * nq;
-        const int nqb = blocks(sq, nq);
-        if (nq != kMaxNQ && rounds((int64_t)nqb * num_heads) * item(nq, skv) < best) {
-            best = rounds((int64_t)nqb * num_heads) * item(nq, skv);
-            p = AttnPlan{sq, 1, 0, 0, 0, nq, nq};
-        }
-        const int tb_max = (int)std::min<int64_t>(nqb, 2 * C / num_heads + 1);
-        for (int tb = 1; tb <= nqb; ++tb) {
-            if (tb > tb_max && tb != nqb) continue;
-            const int main_rows = (nqb - tb) * bq;
-            const int tail_rows = sq - main_rows;
-            const double t_main = rounds((int64_t)(nqb - tb) * num_heads) * item(nq, skv);
-            for (int tq = kMaxNQ; tq >= 2; --tq) {
-                const int ntb = blocks(tail_rows, tq);
-                if (tq != nq) {  // the tail over all keys straight into the outputs: one more launch
-                    const double t = t_main + rounds((int64_t)ntb * num_heads) * item(tq, skv) + 0.5 * kExtraLaunch;
-                    if (t < best) {
-                        best = t;
-                        p = AttnPlan{main_rows, 1, 0, 0, 0, nq, tq};
-                    }
-                }
-                if (skv < 2 * kMinSplitKeys) continue;
-                for (int k = 2; k <= kMaxSplit; ++k) {
-                    const int len = ((skv + k - 1) / k + BN - 1) / BN * BN;
-                    if (len < kMinSplitKeys) break;
-                    const int ke = (skv + len - 1) / len;
-                    const int64_t o_el = (int64_t)ke * num_heads * tail_rows * D;
-                    if (o_el > max_o_elems) break;
-                    const double merge = ((double)o_el * 8.0 + (double)num_heads * tail_rows * D * 2.0) / kMergeBw;
-                    const double t =
-                        t_main + rounds((int64_t)ntb * num_heads * ke) * item(tq, len) + merge + kExtraLaunch;
-                    if (t < best) {
-                        best = t;
-                        p = AttnPlan{main_rows, ke, len, o_el, (int64_t)ke * num_heads * tail_rows, nq, tq};
-                    }
-                }
-            }
-        }
-    }
-    return p;
+    return plan_attention(cu_count(), num_heads, sq, skv, max_o_elems);
 }
 
 hipError_t launch_attention_f16(const FlashArgs &args, const AttnPlan &p, float *ws_o, float *ws_lse,

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "fastdiv.hpp"
+#include "launch_plan.hpp"
 
 namespace attnblk {
 
@@ -144,20 +145,6 @@ struct MergeArgs {
     int out_f16;
     float *lse_out;
     int64_t lse_hs;  // head stride of lse_out; 0 means sq
-};
-
-// Launch plan of one fp16 attention (flash_fwd.hip): the query rows
-// [0, main_rows) of every head run as whole-key workgroups of nq query blocks
-// per wave; the rows [main_rows, sq) (the tail) run in workgroups of tail_nq
-// blocks per wave, over all keys straight into the outputs (n_split <= 1), or
-// split into n_split key ranges of split_len keys whose fp32 partials
-// (o_elems and lse_elems floats of workspace) are then merged into the
-// outputs. main_rows == sq: one plain launch.
-struct AttnPlan {
-    int main_rows, n_split, split_len;
-    int64_t o_elems, lse_elems;
-    int nq;       // 16-row query blocks per wave of the whole-key launch (3: 384-row workgroups, 2: 256)
-    int tail_nq;  // the same for the rows from main_rows on
 };
 
 // Workspace budgets of a key-split attention tail (floats of partial rows):
